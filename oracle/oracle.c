@@ -1,0 +1,439 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for leak-free causal MXFP8 attention.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h): used by the tests, the smoke check
+ * and the benchmark's CPU-baseline leg, never by the product path.
+ *
+ * Everything here is written for a reader checking it against the pages by
+ * eye: fp64 arithmetic, no blocking, no SIMD, OpenMP only across output rows.
+ * Citations name the page and its section:
+ *   [TE#3865 Description]  TransformerEngine PR #3865, section "Description"
+ *   [TE#3865 commit]       the same PR's own commit message
+ *   [cuDNN-FE#1088 summary] cudnn-frontend PR #1088, the PR summary
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   R1  E8M0 rule: the smallest power of two 2^k with amax <= 448 * 2^k, so no
+ *       element saturates; an all-zero block gets k = -127 (byte 0).
+ *   R2  Element rounding: OCP E4M3FN grid (max 448), round to nearest, ties to
+ *       even, saturating, sign of zero kept (negative -> 0x80).
+ *   R5  "one power-of-two amplitude per token": one E8M0 per (b, s, kv-head)
+ *       over all D, rule R1, and the normalised copy stored as E4M3 codes.
+ *   R6  P of the completed blocks is quantised with one E8M0 per (query row,
+ *       32-key block aligned to multiples of 32) on p = 2^(t - T), T an integer
+ *       upper bound of the row's max of t = scale*log2(e)*q.k; the normaliser l
+ *       sums the unquantised p. The code of p is decided on p rounded to fp32,
+ *       the precision in which the GPU kernel holds P.
+ *   R7  Own block: s = scale * q.k on decoded MXFP8 Q/K, p = e^(s - max s) in
+ *       full precision (not quantised), V from the token-normalised copy.
+ *   R8  A row with no completed key (i < 32) has O_c = 0, lse_c = -inf.
+ *   R9  GQA: q-head hq reads kv-head floor(hq / (Hq / Hkv)).
+ */
+#include "oracle.h"
+
+#include <assert.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define LN2 0.69314718055994530942
+#define LOG2E 1.44269504088896340736
+
+/* ---------------------------------------------------------------- codec --- */
+
+/* O1 -- E8M0 exponent [cuDNN-FE#1088 summary: "one UE8M0 scale per 32"],
+   rule R1: amax = f * 2^E with f in [1, 2); k = E - 8 when f <= 1.75, else
+   E - 7, which is the least k with amax <= 448 * 2^k = 1.75 * 2^(k+8). */
+int orc_e8m0_exponent(double amax) {
+  assert(amax >= 0.0 && isfinite(amax));
+  if (amax == 0.0) return -127;
+  int e2;
+  double m = frexp(amax, &e2); /* amax = m * 2^e2, m in [0.5, 1) */
+  double f = 2.0 * m;          /* f in [1, 2) */
+  int E = e2 - 1;
+  int k = E - 8 + (f > 1.75 ? 1 : 0);
+  if (k < -127) k = -127;
+  if (k > 127) k = 127;
+  return k;
+}
+
+/* O2 -- E4M3 encode (rule R2). Normal codes are 1.mmm * 2^(e-7), e = 1..15,
+   the largest finite one is e = 15, m = 6 (448 = 0x7E); subnormals are
+   0.mmm * 2^-6 (step 2^-9). The code's integer order follows its magnitude, so
+   a mantissa carry into the exponent is just code + 1. */
+uint8_t orc_e4m3_encode(double y) {
+  assert(!isnan(y));
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs(y);
+  int code;
+  if (a >= 448.0) {
+    code = 0x7E;
+  } else if (a < 0.015625) { /* below 2^-6: subnormal grid, step 2^-9 */
+    code = (int)nearbyint(a * 512.0); /* 0..8; 8 is the smallest normal */
+  } else {
+    int e2;
+    double m = frexp(a, &e2);
+    int E = e2 - 1;                         /* a = f * 2^E, f in [1, 2) */
+    double frac = (2.0 * m - 1.0) * 8.0;    /* mantissa in units of 2^-3 */
+    int mant = (int)nearbyint(frac);        /* ties to even */
+    code = ((E + 7) << 3) + mant;           /* mant == 8 carries into e */
+    if (code > 0x7E) code = 0x7E;
+  }
+  return (uint8_t)(sign | code);
+}
+
+/* O3 -- E4M3 decode. */
+double orc_e4m3_decode(uint8_t c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(8.0 + m, e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+static double mx_value(uint8_t code, uint8_t scale_byte) {
+  return ldexp(orc_e4m3_decode(code), (int)scale_byte - 127);
+}
+
+static double bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* One MX block: n values -> scale byte and n codes. */
+static uint8_t mx_block(const double* x, int n, uint8_t* codes_out, int64_t code_stride) {
+  double amax = 0.0;
+  for (int r = 0; r < n; ++r) amax = fmax(amax, fabs(x[r]));
+  int k = orc_e8m0_exponent(amax);
+  for (int r = 0; r < n; ++r) codes_out[r * code_stride] = orc_e4m3_encode(ldexp(x[r], -k));
+  return (uint8_t)(k + 127);
+}
+
+/* ----------------------------------------------------------- quantisers --- */
+
+/* O4 -- rowwise along D for Q and K [TE#3865 Description: backward on "Q/K
+   decoded from their rowwise MXFP8 bytes"]: block g of row (b,s,h) is
+   d in [32g, 32g+32). */
+void orc_quantize_rowwise(const uint16_t* x, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
+                          uint8_t* codes, uint8_t* scales) {
+  assert(D % 32 == 0);
+  const int G = D / 32;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b)
+    for (int s = 0; s < S; ++s)
+      for (int h = 0; h < H; ++h) {
+        double blk[32];
+        const uint16_t* row = x + b * sb + s * ss + h * sh;
+        int64_t out_row = (((int64_t)b * H + h) * S + s);
+        for (int g = 0; g < G; ++g) {
+          for (int r = 0; r < 32; ++r) blk[r] = bf16_value(row[32 * g + r]);
+          scales[out_row * G + g] = mx_block(blk, 32, codes + out_row * D + 32 * g, 1);
+        }
+      }
+}
+
+/* O5 -- V columnwise: block u of column (b,h,d) is tokens [32u, 32u+32)
+   [TE#3865 Description: "A columnwise MXFP8 V scale is shared by 32
+   consecutive tokens"]. O6 -- the token-normalised copy: one amplitude per
+   (b,s,h) over all D [TE#3865 Description: "one power-of-two amplitude per
+   token"], reading R5. */
+void orc_quantize_v(const uint16_t* v, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
+                    uint8_t* col_codes, uint8_t* col_scales, uint8_t* tn_codes, uint8_t* tn_amps) {
+  assert(S % 32 == 0);
+  const int U = S / 32;
+  if (col_codes && col_scales) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < H; ++h)
+        for (int u = 0; u < U; ++u)
+          for (int d = 0; d < D; ++d) {
+            double blk[32];
+            for (int r = 0; r < 32; ++r) blk[r] = bf16_value(v[b * sb + (int64_t)(32 * u + r) * ss + h * sh + d]);
+            int64_t col = ((int64_t)b * H + h) * D + d; /* codes [B,H,D,S] */
+            col_scales[(((int64_t)b * H + h) * U + u) * D + d] =
+                mx_block(blk, 32, col_codes + col * S + 32 * u, 1);
+          }
+  }
+  if (tn_codes && tn_amps) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < H; ++h)
+        for (int s = 0; s < S; ++s) {
+          double* row = (double*)malloc(sizeof(double) * D);
+          for (int d = 0; d < D; ++d) row[d] = bf16_value(v[b * sb + (int64_t)s * ss + h * sh + d]);
+          int64_t r = ((int64_t)b * H + h) * S + s;
+          tn_amps[r] = mx_block(row, D, tn_codes + r * D, 1);
+          free(row);
+        }
+  }
+}
+
+/* ------------------------------------------------------ decoded operands --- */
+
+/* Decoded operand tensors, all token-major [B,H,S,D] in fp64. */
+static double* decode_rowwise(const uint8_t* c, const uint8_t* s, int B, int H, int S, int D) {
+  int64_t n = (int64_t)B * H * S * D;
+  double* out = (double*)malloc(sizeof(double) * n);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = mx_value(c[i], s[i / 32]);
+  return out;
+}
+
+static double* decode_vcol(const uint8_t* c, const uint8_t* s, int B, int H, int S, int D) {
+  const int U = S / 32;
+  double* out = (double*)malloc(sizeof(double) * (int64_t)B * H * S * D);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int t = 0; t < S; ++t)
+        for (int d = 0; d < D; ++d) {
+          int64_t bh = (int64_t)b * H + h;
+          out[(bh * S + t) * D + d] = mx_value(c[(bh * D + d) * S + t], s[(bh * U + t / 32) * D + d]);
+        }
+  return out;
+}
+
+static double* decode_vtn(const uint8_t* c, const uint8_t* a, int B, int H, int S, int D) {
+  int64_t n = (int64_t)B * H * S * D;
+  double* out = (double*)malloc(sizeof(double) * n);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = mx_value(c[i], a[i / D]);
+  return out;
+}
+
+static double* bf16_tensor(const uint16_t* x, int64_t sb, int64_t ss, int64_t sh, int B, int S, int H, int D) {
+  double* out = (double*)malloc(sizeof(double) * (int64_t)B * H * S * D);
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int s = 0; s < S; ++s)
+        for (int d = 0; d < D; ++d)
+          out[((((int64_t)b * H + h) * S) + s) * D + d] = bf16_value(x[b * sb + s * ss + h * sh + d]);
+  return out;
+}
+
+static double dot(const double* a, const double* b, int D) {
+  double acc = 0.0;
+  for (int d = 0; d < D; ++d) acc += a[d] * b[d];
+  return acc;
+}
+
+/* MX quantise-dequantise of one block of P (reading R6): the code is decided on
+   each p rounded to fp32, and the block scale on the fp32 maximum. */
+static void quantize_p_block(const double* p, double* phat, int n) {
+  double amax = 0.0;
+  for (int r = 0; r < n; ++r) amax = fmax(amax, (double)(float)p[r]);
+  int k = orc_e8m0_exponent(amax);
+  for (int r = 0; r < n; ++r) phat[r] = ldexp(orc_e4m3_decode(orc_e4m3_encode(ldexp((double)(float)p[r], -k))), k);
+}
+
+/* ------------------------------------------------------- partial kernels --- */
+
+/* O7 -- completed-block partial of one query row [TE#3865 Description, first
+   bullet: keys j < 32 * floor(i / 32)], or, with `leaky`, the ordinary causal
+   MXFP8 row over j <= i. Keys [0, n) with n as above; P blocks are the 32-key
+   blocks aligned to multiples of 32 (the last one partial when leaky).
+   quantize_p = 0 replaces the P quantiser by the identity. */
+static void completed_row(const double* q, const double* K, const double* V, int i, int D, double sigma,
+                          int quantize_p, int t_shift, int leaky, double* o, double* lse) {
+  int n = leaky ? i + 1 : 32 * (i / 32);
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (n == 0) { /* R8 */
+    *lse = -INFINITY;
+    return;
+  }
+  double* t = (double*)malloc(sizeof(double) * n);
+  double* p = (double*)malloc(sizeof(double) * n);
+  double* phat = (double*)malloc(sizeof(double) * n);
+  double tmax = -INFINITY;
+  for (int j = 0; j < n; ++j) {
+    t[j] = sigma * LOG2E * dot(q, K + (int64_t)j * D, D);
+    tmax = fmax(tmax, t[j]);
+  }
+  double T = ceil(tmax) + t_shift; /* integer exponent offset */
+  double l = 0.0;
+  for (int j = 0; j < n; ++j) {
+    p[j] = exp2(t[j] - T);
+    l += p[j];
+  }
+  for (int u0 = 0; u0 < n; u0 += 32) {
+    int m = (n - u0 < 32) ? n - u0 : 32;
+    if (quantize_p)
+      quantize_p_block(p + u0, phat + u0, m);
+    else
+      for (int r = 0; r < m; ++r) phat[u0 + r] = p[u0 + r];
+  }
+  for (int j = 0; j < n; ++j)
+    for (int d = 0; d < D; ++d) o[d] += phat[j] * V[(int64_t)j * D + d];
+  for (int d = 0; d < D; ++d) o[d] /= l;
+  *lse = LN2 * (T + log2(l));
+  free(t);
+  free(p);
+  free(phat);
+}
+
+/* O8 -- own-block partial of one query row [TE#3865 Description, second
+   bullet], reading R7: keys 32*floor(i/32) .. i, full-precision softmax. */
+static void own_row(const double* q, const double* K, const double* Vt, int i, int D, double sigma, double* o,
+                    double* lse) {
+  int j0 = 32 * (i / 32);
+  double s[32], p[32];
+  double m = -INFINITY;
+  for (int j = j0; j <= i; ++j) {
+    s[j - j0] = sigma * dot(q, K + (int64_t)j * D, D);
+    m = fmax(m, s[j - j0]);
+  }
+  double l = 0.0;
+  for (int j = j0; j <= i; ++j) {
+    p[j - j0] = exp(s[j - j0] - m);
+    l += p[j - j0];
+  }
+  for (int d = 0; d < D; ++d) {
+    double acc = 0.0;
+    for (int j = j0; j <= i; ++j) acc += p[j - j0] * Vt[(int64_t)j * D + d];
+    o[d] = acc / l;
+  }
+  *lse = m + log(l);
+}
+
+/* O9 -- merge through the log-sum-exps [TE#3865 Description, second bullet:
+   "merged with the cuDNN partial through the two log-sum-exps"]. */
+static void merge_row(const double* oc, double lc, const double* oo, double lo, int D, double* o, double* lse) {
+  double M = fmax(lc, lo);
+  double wc = (lc == -INFINITY) ? 0.0 : exp(lc - M);
+  double wo = (lo == -INFINITY) ? 0.0 : exp(lo - M);
+  for (int d = 0; d < D; ++d) o[d] = (wc * oc[d] + wo * oo[d]) / (wc + wo);
+  *lse = M + log(wc + wo);
+}
+
+void orc_lse_merge(const double* oc, const double* lsec, const double* oo, const double* lseo, int64_t n, int D,
+                   double* o, double* lse) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) merge_row(oc + r * D, lsec[r], oo + r * D, lseo[r], D, o + r * D, lse + r);
+}
+
+/* --------------------------------------------------------- row drivers --- */
+
+enum { PART_COMPLETED, PART_LEAKY, PART_OWN, PART_TEXTBOOK };
+
+static int row_index(const int32_t* rows, int r) { return rows ? rows[r] : r; }
+
+/* Runs one partial over every (b, hq, listed row). Q, K, V are decoded
+   token-major [B,H,S,D] tensors. */
+static void run_rows(int part, const double* Q, const double* K, const double* V, int B, int S, int Hq, int Hkv,
+                     int D, float scale, const int32_t* rows, int nrows, int quantize_p, int t_shift, double* o,
+                     double* lse) {
+  assert(Hq % Hkv == 0);
+  const int G = Hq / Hkv;
+  const double sigma = (double)scale;
+  if (!rows) assert(nrows == S);
+#pragma omp parallel for collapse(3) schedule(dynamic, 4)
+  for (int b = 0; b < B; ++b)
+    for (int hq = 0; hq < Hq; ++hq)
+      for (int r = 0; r < nrows; ++r) {
+        int i = row_index(rows, r);
+        assert(i >= 0 && i < S);
+        int hk = hq / G; /* R9 */
+        const double* q = Q + (((int64_t)b * Hq + hq) * S + i) * D;
+        const double* Kh = K + ((int64_t)b * Hkv + hk) * S * D;
+        const double* Vh = V + ((int64_t)b * Hkv + hk) * S * D;
+        int64_t orow = ((int64_t)b * Hq + hq) * nrows + r;
+        if (part == PART_OWN) {
+          own_row(q, Kh, Vh, i, D, sigma, o + orow * D, lse + orow);
+        } else if (part == PART_TEXTBOOK) {
+          double* s = (double*)malloc(sizeof(double) * (i + 1));
+          double m = -INFINITY, l = 0.0;
+          for (int j = 0; j <= i; ++j) {
+            s[j] = sigma * dot(q, Kh + (int64_t)j * D, D);
+            m = fmax(m, s[j]);
+          }
+          for (int d = 0; d < D; ++d) o[orow * D + d] = 0.0;
+          for (int j = 0; j <= i; ++j) {
+            double p = exp(s[j] - m);
+            l += p;
+            for (int d = 0; d < D; ++d) o[orow * D + d] += p * Vh[(int64_t)j * D + d];
+          }
+          for (int d = 0; d < D; ++d) o[orow * D + d] /= l;
+          lse[orow] = m + log(l);
+          free(s);
+        } else {
+          completed_row(q, Kh, Vh, i, D, sigma, quantize_p, t_shift, part == PART_LEAKY, o + orow * D, lse + orow);
+        }
+      }
+}
+
+void orc_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                        const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale,
+                        const int32_t* rows, int nrows, int t_shift, double* o, double* lse) {
+  double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
+  double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
+  double* V = decode_vcol(vc, vcs, B, Hkv, S, D);
+  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, t_shift, o, lse);
+  free(Q);
+  free(K);
+  free(V);
+}
+
+void orc_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                    const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
+                    int nrows, double* o, double* lse) {
+  double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
+  double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
+  double* V = decode_vcol(vc, vcs, B, Hkv, S, D);
+  run_rows(PART_LEAKY, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, 0, o, lse);
+  free(Q);
+  free(K);
+  free(V);
+}
+
+void orc_attn_own(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
+                  const uint8_t* vta, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
+                  int nrows, double* o, double* lse) {
+  double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
+  double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
+  double* V = decode_vtn(vt, vta, B, Hkv, S, D);
+  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, o, lse);
+  free(Q);
+  free(K);
+  free(V);
+}
+
+void orc_attn_reference(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh, const uint16_t* k, int64_t ksb,
+                        int64_t kss, int64_t ksh, const uint16_t* v, int64_t vsb, int64_t vss, int64_t vsh, int B,
+                        int S, int Hq, int Hkv, int D, float scale, const int32_t* rows, int nrows, double* o,
+                        double* lse) {
+  double* Q = bf16_tensor(q, qsb, qss, qsh, B, S, Hq, D);
+  double* K = bf16_tensor(k, ksb, kss, ksh, B, S, Hkv, D);
+  double* V = bf16_tensor(v, vsb, vss, vsh, B, S, Hkv, D);
+  run_rows(PART_TEXTBOOK, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, o, lse);
+  free(Q);
+  free(K);
+  free(V);
+}
+
+void orc_attn_identity(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh, const uint16_t* k, int64_t ksb,
+                       int64_t kss, int64_t ksh, const uint16_t* v, int64_t vsb, int64_t vss, int64_t vsh, int B,
+                       int S, int Hq, int Hkv, int D, float scale, const int32_t* rows, int nrows, double* o,
+                       double* lse) {
+  double* Q = bf16_tensor(q, qsb, qss, qsh, B, S, Hq, D);
+  double* K = bf16_tensor(k, ksb, kss, ksh, B, S, Hkv, D);
+  double* V = bf16_tensor(v, vsb, vss, vsh, B, S, Hkv, D);
+  int64_t n = (int64_t)B * Hq * nrows;
+  double* oc = (double*)malloc(sizeof(double) * n * D);
+  double* oo = (double*)malloc(sizeof(double) * n * D);
+  double* lc = (double*)malloc(sizeof(double) * n);
+  double* lo = (double*)malloc(sizeof(double) * n);
+  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, oc, lc);
+  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, oo, lo);
+  orc_lse_merge(oc, lc, oo, lo, n, D, o, lse);
+  free(oc);
+  free(oo);
+  free(lc);
+  free(lo);
+  free(Q);
+  free(K);
+  free(V);
+}

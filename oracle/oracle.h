@@ -1,0 +1,85 @@
+/*
+ * oracle.h -- plain, slow, fp64 CPU model of leak-free causal MXFP8 attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this library: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it. It shares no code with the HIP library.
+ *
+ * What it models (TransformerEngine PR #3865, "[PyTorch] Add causal MXFP8
+ * attention without future-token leakage through V scales", section
+ * "Description" and the PR's commit message):
+ *   - MXFP8: E4M3 element codes with one power-of-two (E8M0) scale per 32
+ *     elements along the contraction axis (cudnn-frontend PR #1088, PR summary).
+ *   - Q and K quantised rowwise along D; V columnwise over 32 tokens.
+ *   - Query i: keys in completed 32-key blocks (j < 32*floor(i/32)) use MXFP8
+ *     P.V with columnwise V scales; its own block (32*floor(i/32) <= j <= i)
+ *     uses a token-normalised V (one power-of-two amplitude per token); the two
+ *     partials are merged through their log-sum-exps.
+ *
+ * Layouts (logical index -> offset) are the ones the C-ABI header documents:
+ *   q/k codes  [B,H,S,D]     q/k scales [B,H,S,D/32]
+ *   v col codes [B,H,D,S]    v col scales [B,H,S/32,D]
+ *   v tn codes  [B,H,S,D]    v tn amplitudes [B,H,S]
+ * bf16 inputs are uint16 bit patterns addressed by element strides
+ * (sb, ss, sh) with unit stride along D.
+ *
+ * Attention entry points compute a list of query rows `rows[0..nrows)` for
+ * every (b, hq); outputs are [B,Hq,nrows,D] and [B,Hq,nrows] in fp64.
+ * rows == NULL means rows 0..S-1 (nrows must then equal S).
+ */
+#ifndef MXFA_ORACLE_H
+#define MXFA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* O1: exponent k of the E8M0 scale for block amax a >= 0 (scale = 2^k). */
+int orc_e8m0_exponent(double amax);
+/* O2: E4M3 (OCP E4M3FN) code of y, round-to-nearest-even, saturating, sign kept. */
+uint8_t orc_e4m3_encode(double y);
+/* O3: value of an E4M3 code (0x7F/0xFF, the NaN codes, decode to NaN). */
+double orc_e4m3_decode(uint8_t code);
+
+/* O4: rowwise MXFP8 of a bf16 tensor [B,S,H,D] (by strides). */
+void orc_quantize_rowwise(const uint16_t* x, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
+                          uint8_t* codes, uint8_t* scales);
+/* O5 + O6: V columnwise over 32 tokens, and the token-normalised copy. Any
+   output pointer may be NULL to skip it. */
+void orc_quantize_v(const uint16_t* v, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
+                    uint8_t* col_codes, uint8_t* col_scales, uint8_t* tn_codes, uint8_t* tn_amps);
+
+/* O7: completed-block partial. t_shift adds an integer to the running
+   exponent T (any integer gives the same result; used as a pin). */
+void orc_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                        const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale,
+                        const int32_t* rows, int nrows, int t_shift, double* o, double* lse);
+/* O8: own-block partial on the token-normalised V. */
+void orc_attn_own(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
+                  const uint8_t* vta, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
+                  int nrows, double* o, double* lse);
+/* O9: merge two partials through their log-sum-exps; n rows of D. */
+void orc_lse_merge(const double* oc, const double* lsec, const double* oo, const double* lseo, int64_t n, int D,
+                   double* o, double* lse);
+
+/* Ordinary ("leaky") causal MXFP8: every key j <= i through the O7 machinery
+   with the columnwise V, whose own-block scale also covers future tokens. */
+void orc_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                    const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
+                    int nrows, double* o, double* lse);
+/* Unquantised textbook causal softmax attention on the bf16 values. */
+void orc_attn_reference(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh, const uint16_t* k, int64_t ksb,
+                        int64_t kss, int64_t ksh, const uint16_t* v, int64_t vsb, int64_t vss, int64_t vsh, int B,
+                        int S, int Hq, int Hkv, int D, float scale, const int32_t* rows, int nrows, double* o,
+                        double* lse);
+/* The split-and-merge structure with every quantiser replaced by the identity. */
+void orc_attn_identity(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh, const uint16_t* k, int64_t ksb,
+                       int64_t kss, int64_t ksh, const uint16_t* v, int64_t vsb, int64_t vss, int64_t vsh, int B,
+                       int S, int Hq, int Hkv, int D, float scale, const int32_t* rows, int nrows, double* o,
+                       double* lse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

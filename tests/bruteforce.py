@@ -1,0 +1,142 @@
+"""Independent brute-force checks that pin the oracle (numpy only; shares nothing with oracle/).
+
+The MXFP8 format (E4M3 elements, one power-of-two E8M0 scale per 32 elements) is stated in
+cudnn-frontend PR #1088 (PR summary) and TransformerEngine PR #3865 (section "Description"). Here
+every rule is evaluated by search instead of by formula:
+  * the E4M3 grid is enumerated from the bit layout (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal; 0x7F/0xFF are NaN), and a value is encoded as the nearest grid
+    point (ties to the even code, magnitudes above the largest finite value saturate, sign kept);
+  * the E8M0 exponent is the smallest integer k in [-127, 127] with amax <= 448 * 2^k;
+  * attention is evaluated in closed form (one expression per row, no running max, no merge).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def e4m3_table() -> np.ndarray:
+    """Value of each of the 256 codes (NaN for 0x7F and 0xFF), from the bit layout."""
+    vals = np.empty(256)
+    for c in range(256):
+        sign = -1.0 if c >> 7 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * (m / 8.0) * 2.0 ** (1 - 7)
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_TAB = e4m3_table()
+_POS_CODES = np.array([c for c in range(0x7F)])  # 0x00..0x7E: every finite non-negative code
+_POS_VALS = _TAB[_POS_CODES]
+assert np.all(np.diff(_POS_VALS) > 0)
+MAX_E4M3 = _POS_VALS[-1]  # 448
+
+
+def encode_nearest(y: np.ndarray) -> np.ndarray:
+    """Nearest-grid-point E4M3 code of each y (ties to the even code, saturating, sign kept)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(_POS_VALS, a, side="left"), 0, len(_POS_VALS) - 1)
+    lo = np.clip(hi - 1, 0, len(_POS_VALS) - 1)
+    d_hi = np.abs(_POS_VALS[hi] - a)
+    d_lo = np.abs(a - _POS_VALS[lo])
+    pick = np.where(d_lo < d_hi, lo, hi)
+    tie = (d_lo == d_hi) & (lo != hi)
+    pick = np.where(tie, np.where(_POS_CODES[lo] % 2 == 0, lo, hi), pick)
+    pick = np.where(a >= MAX_E4M3, len(_POS_VALS) - 1, pick)
+    code = _POS_CODES[pick].astype(np.uint8)
+    return np.where(np.signbit(y), code | 0x80, code).astype(np.uint8)
+
+
+_K = np.arange(-127, 128)
+
+
+def e8m0_search(amax: np.ndarray) -> np.ndarray:
+    """Smallest k in [-127, 127] with amax <= 448 * 2^k (k = -127 if none smaller fits)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    fits = amax[..., None] <= MAX_E4M3 * np.ldexp(1.0, _K)
+    return np.where(fits.any(-1), _K[np.argmax(fits, axis=-1)], 127)
+
+
+def mx_quantize(x: np.ndarray, axis: int) -> tuple[np.ndarray, np.ndarray]:
+    """MX-quantise blocks lying along ``axis`` (the whole axis is one block): (codes, k)."""
+    k = e8m0_search(np.max(np.abs(x), axis=axis, keepdims=True))
+    return encode_nearest(x * np.ldexp(1.0, -k)), k
+
+
+def mx_dequantize(codes: np.ndarray, k: np.ndarray) -> np.ndarray:
+    return _TAB[codes] * np.ldexp(1.0, k)
+
+
+def mx_qdq(x: np.ndarray, axis: int) -> np.ndarray:
+    c, k = mx_quantize(x, axis)
+    return mx_dequantize(c, k)
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def decoded_operands(q, k, v):
+    """Q̂, K̂ (rowwise, 32 along D), V̂col (32 along tokens) and V̂t (one block per token over D),
+    each [B,S,H,D] float64, from bf16 [B,S,H,D] bit patterns, by brute force."""
+    Q, K, V = bf16_values(q), bf16_values(k), bf16_values(v)
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    Qh = mx_qdq(Q.reshape(B, S, Hq, D // 32, 32), axis=-1).reshape(Q.shape)
+    Kh = mx_qdq(K.reshape(B, S, Hkv, D // 32, 32), axis=-1).reshape(K.shape)
+    Vcol = mx_qdq(V.reshape(B, S // 32, 32, Hkv, D), axis=2).reshape(V.shape)
+    Vt = mx_qdq(V, axis=-1)
+    return Qh, Kh, Vcol, Vt
+
+
+def closed_form_forward(q, k, v, scale: float, p_fp32: bool = True):
+    """Leak-free output in closed form, all rows, fp64: for query i with n = 32*floor(i/32),
+
+        O_i = ( sum_{j<n} q_u(e^{s_j}) * V̂col_j + sum_{n<=j<=i} e^{s_j} * V̂t_j ) / sum_{j<=i} e^{s_j}
+
+    with s_j = scale * Q̂_i . K̂_j and q_u the MX quantise-dequantise of the 32 values {e^{s_j}}
+    of key block u (the values rounded to fp32 first when ``p_fp32``). Returns O [B,Hq,S,D]."""
+    Qh, Kh, Vcol, Vt = decoded_operands(q, k, v)
+    B, S, Hq, D = Qh.shape
+    Hkv = Kh.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, S, D))
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            s = float(np.float32(scale)) * (Qh[b, :, hq] @ Kh[b, :, hk].T)  # [S,S]
+            e = np.exp(s)
+            for i in range(S):
+                n = 32 * (i // 32)
+                num = np.zeros(D)
+                if n:
+                    p = e[i, :n].astype(np.float32).astype(np.float64) if p_fp32 else e[i, :n]
+                    ph = mx_qdq(p.reshape(-1, 32), axis=-1).reshape(-1)
+                    num += ph @ Vcol[b, :n, hk]
+                num += e[i, n:i + 1] @ Vt[b, n:i + 1, hk]
+                out[b, hq, i] = num / e[i, :i + 1].sum()
+    return out
+
+
+def textbook_attention(q, k, v, scale: float):
+    """Causal softmax attention in fp64 on the bf16 values (no quantisation). O [B,Hq,S,D], lse [B,Hq,S]."""
+    Q, K, V = bf16_values(q), bf16_values(k), bf16_values(v)
+    B, S, Hq, D = Q.shape
+    G = Hq // K.shape[2]
+    out = np.zeros((B, Hq, S, D))
+    lse = np.zeros((B, Hq, S))
+    mask = np.tril(np.ones((S, S), bool))
+    for b in range(B):
+        for hq in range(Hq):
+            s = float(np.float32(scale)) * (Q[b, :, hq] @ K[b, :, hq // G].T)
+            s = np.where(mask, s, -np.inf)
+            m = s.max(-1, keepdims=True)
+            w = np.exp(s - m)
+            out[b, hq] = (w @ V[b, :, hq // G]) / w.sum(-1, keepdims=True)
+            lse[b, hq] = (m[:, 0] + np.log(w.sum(-1)))
+    return out, lse

@@ -1,0 +1,172 @@
+"""Pins of the oracle's attention (O7 completed partial, O8 own partial, O9 merge) against closed
+forms, special cases, invariants and brute force (tests/bruteforce.py). Nothing here re-types the
+oracle's own formulas: each check is a different route to a value the method fixes."""
+import numpy as np
+import pytest
+
+import bruteforce as bf
+import oracle
+from causal_mxfp8_block_amd.inputs import bf16_bits, custom, make_inputs, perturb_after
+
+SCALE = float(np.float32(1 / np.sqrt(128)))
+
+
+def _inputs(S=128, Hq=1, Hkv=1, seed=0, values="normal", B=1):
+    return make_inputs(custom(B, Hq, Hkv, S, values=values, seed=seed))
+
+
+def _rel(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+def test_identity_variant_is_textbook_attention():
+    """(i) With every quantiser the identity, split + merge equals plain causal softmax attention:
+    pins the masks, the scale, the GQA head map and the merge."""
+    inp = _inputs(S=160, Hq=4, Hkv=2, seed=3, B=2)
+    o, lse = oracle.attn_identity(inp.q, inp.k, inp.v, SCALE)
+    ot, lset = bf.textbook_attention(inp.q, inp.k, inp.v, SCALE)
+    assert _rel(o, ot) < 1e-12
+    assert np.max(np.abs(lse - lset)) < 1e-12
+    o2, lse2 = oracle.attn_reference(inp.q, inp.k, inp.v, SCALE)
+    assert _rel(o2, ot) < 1e-12 and np.max(np.abs(lse2 - lset)) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_forward_matches_closed_form(seed):
+    """(ii)/(vi) The merged output equals the T-free closed form of the method, evaluated by brute
+    force on tiny inputs."""
+    inp = _inputs(S=128, seed=seed)
+    o, lse, _ = oracle.forward(inp.q, inp.k, inp.v, SCALE)
+    ref = bf.closed_form_forward(inp.q, inp.k, inp.v, SCALE)
+    assert _rel(o, ref) < 1e-12
+
+
+def test_forward_matches_closed_form_gqa_outliers():
+    inp = _inputs(S=96, Hq=4, Hkv=2, seed=21, values="outliers")
+    o, _, _ = oracle.forward(inp.q, inp.k, inp.v, SCALE)
+    assert _rel(o, bf.closed_form_forward(inp.q, inp.k, inp.v, SCALE)) < 1e-12
+
+
+def test_zero_query_gives_plain_mean():
+    """(iii) Q = 0: every score is 0, so every p is 1 and O_i is the plain mean of the decoded V rows
+    it sees: V̂col for completed keys, V̂t for its own block."""
+    inp = _inputs(S=96, seed=4)
+    q = np.zeros_like(inp.q)
+    o, _, _ = oracle.forward(q, inp.k, inp.v, SCALE)
+    _, _, vcol, vt = bf.decoded_operands(q, inp.k, inp.v)
+    for i in range(96):
+        n = 32 * (i // 32)
+        rows = np.concatenate([vcol[0, :n, 0], vt[0, n:i + 1, 0]])
+        assert np.allclose(o[0, 0, i], rows.mean(0), rtol=1e-13, atol=1e-15)
+
+
+def test_single_block_is_own_block_only():
+    """(iv) S = 32: no key is completed, so lse_c = -inf and O equals the own-block partial."""
+    inp = _inputs(S=32, seed=5)
+    o, lse, parts = oracle.forward(inp.q, inp.k, inp.v, SCALE)
+    assert np.all(np.isneginf(parts["lse_c"])) and np.all(parts["o_c"] == 0)
+    assert np.array_equal(o, parts["o_o"]) and np.array_equal(lse, parts["lse_o"])
+    # and the own block is plain softmax over keys 0..i on the decoded operands
+    qh, kh, _, vt = bf.decoded_operands(inp.q, inp.k, inp.v)
+    s = SCALE * qh[0, :, 0] @ kh[0, :, 0].T
+    s = np.where(np.tril(np.ones((32, 32), bool)), s, -np.inf)
+    w = np.exp(s - s.max(-1, keepdims=True))
+    assert _rel(o[0, 0], (w @ vt[0, :, 0]) / w.sum(-1, keepdims=True)) < 1e-13
+
+
+@pytest.mark.parametrize("shift", [3, -2, 40])
+def test_running_exponent_shift_invariance(shift):
+    """(v) Any integer T gives the same P codes (E8M0 scaling commutes with powers of two), so the
+    completed partial does not depend on T."""
+    inp = _inputs(S=256, Hq=2, Hkv=1, seed=6)
+    z = oracle.quantize_all(inp.q, inp.k, inp.v)
+    o0, l0 = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 2, 1, SCALE)
+    o1, l1 = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 2, 1, SCALE, t_shift=shift)
+    assert _rel(o1[:, :, 32:], o0[:, :, 32:]) < 1e-14
+    assert np.max(np.abs(l1[:, :, 32:] - l0[:, :, 32:])) < 1e-12
+
+
+def test_row_subset_matches_all_rows():
+    inp = _inputs(S=192, Hq=2, Hkv=2, seed=7)
+    rows = [0, 31, 32, 33, 100, 191]
+    o, lse, _ = oracle.forward(inp.q, inp.k, inp.v, SCALE)
+    o2, lse2, _ = oracle.forward(inp.q, inp.k, inp.v, SCALE, rows=rows)
+    assert np.array_equal(o[:, :, rows], o2) and np.array_equal(lse[:, :, rows], lse2)
+
+
+def test_causality_every_t_tiny():
+    """(vii) Re-randomising every token after t leaves rows 0..t bit-identical, for every t."""
+    inp = _inputs(S=128, seed=0)
+    o0, l0, _ = oracle.forward(inp.q, inp.k, inp.v, SCALE)
+    for t in range(127):
+        pert = perturb_after(inp, t, outlier_at_next=(t % 2 == 0))
+        o1, l1, _ = oracle.forward(pert.q, pert.k, pert.v, SCALE)
+        assert np.array_equal(o0[:, :, :t + 1], o1[:, :, :t + 1]), t
+        assert np.array_equal(l0[:, :, :t + 1], l1[:, :, :t + 1]), t
+
+
+def test_leaky_variant_fails_causality():
+    """(viii) Negative control: ordinary causal MXFP8 changes rows <= t when a x64 outlier is planted
+    at t+1 inside t's own block (it raises that block's shared columnwise V scales), so the causality
+    test has teeth. A x64 outlier only moves the rounding of visible values that fall into the E4M3
+    subnormal range, so not every t shows it; most do. At block boundaries (t = 32c + 31) the
+    ordinary variant is causal too, since no visible token shares a V scale with a later one."""
+    inp = _inputs(S=128, seed=0)
+    a, _ = oracle.forward_leaky(inp.q, inp.k, inp.v, SCALE)
+    leaks, inside = 0, 0
+    for t in range(127):
+        pert = perturb_after(inp, t, outlier_at_next=True)
+        b, _ = oracle.forward_leaky(pert.q, pert.k, pert.v, SCALE)
+        changed = not np.array_equal(a[:, :, :t + 1], b[:, :, :t + 1])
+        if t % 32 == 31:
+            assert not changed, t
+        else:
+            inside += 1
+            leaks += int(changed)
+    assert leaks >= inside // 2, (leaks, inside)
+
+
+def test_bshd_equals_sbhd():
+    """(ix) The same logical draw in BSHD and SBHD gives identical outputs."""
+    a = make_inputs(custom(2, 2, 1, 96, layout="bshd", seed=9))
+    b = make_inputs(custom(2, 2, 1, 96, layout="sbhd", seed=9))
+    oa, la, _ = oracle.forward(a.q, a.k, a.v, SCALE)
+    ob, lb, _ = oracle.forward(oracle.BF16View.sbhd(b.q), oracle.BF16View.sbhd(b.k), oracle.BF16View.sbhd(b.v), SCALE)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_gqa_equals_repeated_kv():
+    """(x) GQA with G q-heads per kv-head equals MHA with each kv-head repeated G times."""
+    inp = _inputs(S=96, Hq=4, Hkv=2, seed=10)
+    o, lse, _ = oracle.forward(inp.q, inp.k, inp.v, SCALE)
+    k2 = np.ascontiguousarray(np.repeat(inp.k, 2, axis=2))
+    v2 = np.ascontiguousarray(np.repeat(inp.v, 2, axis=2))
+    o2, lse2, _ = oracle.forward(inp.q, k2, v2, SCALE)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_merge_closed_form():
+    """O9: merging through the LSEs equals the exp-weighted combination of the two partials."""
+    rng = np.random.default_rng(12)
+    oc, oo = rng.standard_normal((2, 50, 128))
+    lc, lo = rng.standard_normal((2, 50)) * 5
+    lc[:7] = -np.inf  # rows with no completed key (R8)
+    o, lse = oracle.lse_merge(oc, lc, oo, lo)
+    num = np.exp(lc)[:, None] * oc + np.exp(lo)[:, None] * oo
+    den = np.exp(lc) + np.exp(lo)
+    assert _rel(o, num / den[:, None]) < 1e-13
+    assert np.max(np.abs(lse - np.log(den))) < 1e-13
+    assert np.array_equal(o[:7], oo[:7]) and np.array_equal(lse[:7], lo[:7])
+
+
+def test_leaky_differs_from_leak_free_only_inside_blocks():
+    """The leaky variant reads V̂col for the own block; it agrees with the leak-free output at the
+    identity quantiser's limit (the split itself is exact), and its rows differ from the leak-free
+    rows on real data."""
+    inp = _inputs(S=128, seed=1)
+    o, _, _ = oracle.forward(inp.q, inp.k, inp.v, SCALE)
+    ol, _ = oracle.forward_leaky(inp.q, inp.k, inp.v, SCALE)
+    assert not np.array_equal(o, ol)
+    ref, _ = bf.textbook_attention(inp.q, inp.k, inp.v, SCALE)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(o - ref)) < 0.2 * rms * 10 and np.max(np.abs(ol - ref)) < 0.2 * rms * 10
