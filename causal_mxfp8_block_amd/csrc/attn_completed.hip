@@ -1,0 +1,247 @@
+// attn_completed.hip -- completed-block partial of leak-free causal MXFP8 attention, gfx950.
+//
+// TransformerEngine PR #3865, "Description", first bullet: query i attends in MXFP8 to every key of
+// the 32-token blocks that end at or before its own block, j < 32*floor(i/32); every columnwise V
+// scale read there covers visible tokens only. This is nearly all of the attention FLOPs.
+//
+// Design (CDNA4, wave64):
+//  * A workgroup is 4 waves; wave w owns the 32 queries of one 32-token block, so its key range is
+//    [0, 32*cb) with no per-element mask: the completed-block mask is block-granular.
+//  * Scores are computed transposed, S^T = K . Q^T, with the block-scaled FP8 MFMA
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, one E8M0 per 32 along D on both sides). The
+//    accumulator then holds one query per lane (lane & 31) and 16 keys per 32-key tile, so row
+//    statistics are lane-local up to one exchange with lane ^ 32 (v_permlane32_swap).
+//  * Online softmax in the log2 domain with an integer running exponent T: p = 2^(t - T). T is
+//    raised only when a block maximum would exceed 2^8 (lazy rescale); the E8M0 quantisation of P
+//    commutes with powers of two, so the P codes do not depend on T.
+//  * P is quantised to E4M3 with one E8M0 per (query, 32-key block) by the scaled conversion
+//    v_cvt_scalef32_pk_fp8_f32; four v_permlane32_swaps move the codes into the B-operand layout of
+//    O^T = V^T . P^T (block-scaled FP8 MFMA again, V columnwise codes keys-contiguous per column).
+//  * O^T leaves one query per lane too, so the rescale and the final 1/l are per-lane scalars.
+//  * K and V tiles of 64 keys are staged in LDS once per workgroup and shared by the 4 waves.
+//  * Workgroups are launched longest-first (the causal work of a query tile grows with its index).
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxfa {
+
+constexpr int CB_BM = 128;    // queries per workgroup (4 waves x 32)
+constexpr int CB_BN = 64;     // keys per tile (two 32-key MX blocks)
+constexpr int CB_KROW = 144;  // LDS bytes per K row (128 codes + 16 pad: conflict-free 16-byte reads)
+constexpr int CB_VROW = 80;   // LDS bytes per V column (64 codes + 16 pad)
+constexpr float CB_PMAX_LAZY = 256.0f;  // raise T once a block maximum of p exceeds 2^8
+
+struct __align__(16) CompletedSmem {
+  uint8_t k[CB_BN * CB_KROW];  // K codes, key-major
+  uint8_t v[128 * CB_VROW];    // V codes, column-major (keys contiguous)
+  uint32_t ks[CB_BN];          // the 4 E8M0 bytes of each key
+  uint8_t vs[2 * 128];         // E8M0 bytes of the two key blocks, per column
+};
+
+__device__ __forceinline__ v8i make_v8i(uint4 a, uint4 b) {
+  v8i r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+  return r;
+}
+
+// Exchange with lane ^ 32: returns (x of lanes 0..31, y of lanes 32..63) arranged as the builtin
+// does: after swap(x, y), x in lanes 32..63 and y in lanes 0..31 have traded places.
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
+__global__ __launch_bounds__(256) void completed_kernel(const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs,
+                                                        const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
+                                                        const uint8_t* __restrict__ vc,
+                                                        const uint8_t* __restrict__ vcs, int S, int Hq, int Hkv,
+                                                        float scale_log2, float* __restrict__ o_c,
+                                                        float* __restrict__ lse_c, int n_qtiles) {
+  __shared__ CompletedSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, hf = lane >> 5;
+  const int qtile = n_qtiles - 1 - (int)blockIdx.x;  // longest first
+  const int hq = blockIdx.y, b = blockIdx.z;
+  const int hk = hq / (Hq / Hkv);
+  const int q0 = qtile * CB_BM;
+  const int qw = q0 + 32 * wave;          // first query of this wave; its keys are j < qw
+  const bool wave_valid = qw < S;
+  const int e_w = wave_valid ? qw : 0;
+  const int e_wg = min(q0 + 96, S - 32);  // key range end of the last valid wave
+  const int ntiles = (e_wg + CB_BN - 1) / CB_BN;
+  const int64_t bhq = (int64_t)b * Hq + hq, bhk = (int64_t)b * Hkv + hk;
+
+  // Q^T operand (B of S^T = K Q^T) for the two 64-wide K steps over D. Lane (c, hf) holds bytes
+  // d = 64m + 16hf + [0,16) and 64m + 32 + 16hf + [0,16) of query qw + c; its scale is that of
+  // D-block 2m + hf.
+  v8i qop[2] = {};
+  int qsc[2] = {127, 127};
+  if (wave_valid) {
+    const uint8_t* qrow = qc + (bhq * S + qw + c) * 128;
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(qs + (bhq * S + qw + c) * 4);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      qop[m] = make_v8i(*reinterpret_cast<const uint4*>(qrow + 64 * m + 16 * hf),
+                        *reinterpret_cast<const uint4*>(qrow + 64 * m + 32 + 16 * hf));
+      qsc[m] = (int)((sw >> (8 * (2 * m + hf))) & 0xffu);
+    }
+  }
+
+  v16f oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float T = -INFINITY;  // integer-valued running exponent
+  float lsum = 0.f;     // this lane's share of sum p
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt0 = it * CB_BN;
+    __syncthreads();  // the previous tile has been consumed
+    {
+      const int r = tid >> 2, ch = (tid & 3) * 32;
+      const uint8_t* src = kc + (bhk * S + kt0 + r) * 128 + ch;
+      *reinterpret_cast<uint4*>(sm.k + r * CB_KROW + ch) = *reinterpret_cast<const uint4*>(src);
+      *reinterpret_cast<uint4*>(sm.k + r * CB_KROW + ch + 16) = *reinterpret_cast<const uint4*>(src + 16);
+      const int d = tid >> 1, hv = (tid & 1) * 32;
+      const uint8_t* vsrc = vc + (bhk * 128 + d) * S + kt0 + hv;
+      *reinterpret_cast<uint4*>(sm.v + d * CB_VROW + hv) = *reinterpret_cast<const uint4*>(vsrc);
+      *reinterpret_cast<uint4*>(sm.v + d * CB_VROW + hv + 16) = *reinterpret_cast<const uint4*>(vsrc + 16);
+      if (tid < 64) {
+        sm.ks[tid] = *reinterpret_cast<const uint32_t*>(ks + (bhk * S + kt0 + tid) * 4);
+      } else if (tid < 128) {
+        *reinterpret_cast<uint32_t*>(sm.vs + (tid - 64) * 4) =
+            *reinterpret_cast<const uint32_t*>(vcs + (bhk * (S / 32) + kt0 / 32) * 128 + (tid - 64) * 4);
+      }
+    }
+    __syncthreads();
+    if (kt0 >= e_w) continue;  // wave-uniform: this wave's keys end before the tile
+    const bool second = kt0 + 32 < e_w;  // is the tile's second 32-key block completed for this wave?
+
+    // ---- S^T = K Q^T for the tile's two 32-key blocks --------------------------------------
+    v16f sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+      if (kt == 1 && !second) continue;
+      const uint32_t ksw = sm.ks[32 * kt + c];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint8_t* kr = sm.k + (32 * kt + c) * CB_KROW + 64 * m + 16 * hf;
+        const v8i kop = make_v8i(*reinterpret_cast<const uint4*>(kr), *reinterpret_cast<const uint4*>(kr + 32));
+        const int ksc = (int)((ksw >> (8 * (2 * m + hf))) & 0xffu);
+        sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[m], sacc[kt], 0, 0, 0, ksc, 0, qsc[m]);
+      }
+    }
+    // Lane (c, hf), element i of block kt holds key kt0 + 32kt + 8(i/4) + 4hf + (i%4), query c.
+
+    // ---- p = 2^(t - T), block maxima, lazy rescale ------------------------------------------
+    float p[2][16];
+    float M0 = 0.f, M1 = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+      const float negT = -T;
+      float pm0 = 0.f, pm1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[0][i] = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], scale_log2, negT));
+        pm0 = fmaxf(pm0, p[0][i]);
+        p[1][i] = second ? __builtin_amdgcn_exp2f(fmaf(sacc[1][i], scale_log2, negT)) : 0.f;
+        pm1 = fmaxf(pm1, p[1][i]);
+      }
+      uint32_t x = __builtin_bit_cast(uint32_t, pm0), y = __builtin_bit_cast(uint32_t, pm1);
+      swap32(x, y);  // lanes 0..31 now hold both halves of block 0, lanes 32..63 of block 1
+      uint32_t mo = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y)));
+      uint32_t mo2 = mo;
+      swap32(mo, mo2);  // every lane: mo = block-0 maximum, mo2 = block-1 maximum
+      M0 = __builtin_bit_cast(float, mo);
+      M1 = __builtin_bit_cast(float, mo2);
+      if (!__any(fmaxf(M0, M1) > CB_PMAX_LAZY)) break;
+      // Rare path: raise T to ceil(row max of t); rescale by the exact power of two 2^(T - Tn).
+      float mt = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        mt = fmaxf(mt, sacc[0][i] * scale_log2);
+        if (second) mt = fmaxf(mt, sacc[1][i] * scale_log2);
+      }
+      uint32_t a = __builtin_bit_cast(uint32_t, mt), a2 = a;
+      swap32(a, a2);
+      mt = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, a2));
+      const float Tn = fmaxf(T, ceilf(mt));
+      const float f = __builtin_amdgcn_exp2f(T - Tn);  // 0 on the first tile, else 2^-(integer)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= f;
+      lsum *= f;
+      T = Tn;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lsum += p[0][i] + p[1][i];
+
+    // ---- quantise P: one E8M0 per (query, 32-key block) --------------------------------------
+    // Exponent -127 is only reached by blocks whose largest p is below 2^-118; they use -126 so the
+    // conversion's power-of-two divisor stays a normal fp32 value.
+    const int k0 = max(e8m0_exponent(M0), -126), k1 = max(e8m0_exponent(M1), -126);
+    const float sc0 = u2f((uint32_t)(127 + k0) << 23), sc1 = u2f((uint32_t)(127 + k1) << 23);
+    uint32_t sl[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      sl[g] = pack4_e4m3_scaled(p[0][4 * g], p[0][4 * g + 1], p[0][4 * g + 2], p[0][4 * g + 3], sc0);
+      sl[4 + g] = pack4_e4m3_scaled(p[1][4 * g], p[1][4 * g + 1], p[1][4 * g + 2], p[1][4 * g + 3], sc1);
+    }
+    // Slot g holds keys 8g + 4hf + [0,4) of its block. The B operand of O^T wants, in lane hf,
+    // keys 16hf + [0,16) of block 0 then of block 1: trade slots 2,3 (6,7) of the lower half for
+    // slots 0,1 (4,5) of the upper half.
+    swap32(sl[0], sl[2]);
+    swap32(sl[1], sl[3]);
+    swap32(sl[4], sl[6]);
+    swap32(sl[5], sl[7]);
+    v8i pop;
+    pop[0] = (int)sl[0]; pop[1] = (int)sl[2]; pop[2] = (int)sl[1]; pop[3] = (int)sl[3];
+    pop[4] = (int)sl[4]; pop[5] = (int)sl[6]; pop[6] = (int)sl[5]; pop[7] = (int)sl[7];
+    const int psc = (hf ? k1 : k0) + 127;
+
+    // ---- O^T += V^T P^T over the four 32-column tiles of D -----------------------------------
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint8_t* vr = sm.v + (32 * dt + c) * CB_VROW + 16 * hf;
+      const v8i vop = make_v8i(*reinterpret_cast<const uint4*>(vr), *reinterpret_cast<const uint4*>(vr + 32));
+      const int vsc = sm.vs[hf * 128 + 32 * dt + c];
+      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, oacc[dt], 0, 0, 0, vsc, 0, psc);
+    }
+  }
+
+  // ---- epilogue: O_c = acc / l, lse_c = ln2 (T + log2 l) ---------------------------------------
+  uint32_t la = __builtin_bit_cast(uint32_t, lsum), lb = la;
+  swap32(la, lb);
+  const float ltot = __builtin_bit_cast(float, la) + __builtin_bit_cast(float, lb);
+  if (!wave_valid) return;
+  float* orow = o_c + (bhq * S + qw + c) * 128;
+  const bool empty = (e_w == 0);
+  const float inv = empty ? 0.f : 1.0f / ltot;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // Lane (c, hf), element i of tile dt: column d = 32dt + 8(i/4) + 4hf + (i%4).
+      const float4 val = make_float4(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                                     oacc[dt][4 * g + 3] * inv);
+      *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * hf) = val;
+    }
+  if (hf == 0) lse_c[bhq * S + qw + c] = empty ? -INFINITY : (T + log2f(ltot)) * 0.69314718055994530942f;
+}
+
+hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                 const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv,
+                                 float softmax_scale, float* o_c, float* lse_c, hipStream_t stream) {
+  const int n_qtiles = (S + CB_BM - 1) / CB_BM;
+  const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  completed_kernel<<<dim3((unsigned)n_qtiles, (unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(
+      qc, qs, kc, ks, vc, vcs, S, Hq, Hkv, scale_log2, o_c, lse_c, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace mxfa

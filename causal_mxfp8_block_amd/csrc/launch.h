@@ -1,0 +1,23 @@
+// launch.h -- host-side launchers of the libmxfa kernels (called by api.cpp after validation).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfa {
+
+hipError_t launch_quantize_rowwise(const uint16_t* x, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_v(const uint16_t* v, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
+                             uint8_t* col_codes, uint8_t* col_scales, uint8_t* tn_codes, uint8_t* tn_amps,
+                             hipStream_t stream);
+hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                 const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv,
+                                 float softmax_scale, float* o_c, float* lse_c, hipStream_t stream);
+hipError_t launch_attn_own_block(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                 const uint8_t* vt, const uint8_t* vta, int B, int S, int Hq, int Hkv,
+                                 float softmax_scale, float* o_o, float* lse_o, hipStream_t stream);
+hipError_t launch_lse_merge(const float* o_c, const float* lse_c, const float* o_o, const float* lse_o, int B, int S,
+                            int H, void* out, int64_t osb, int64_t oss, int64_t osh, int out_bf16, float* lse_out,
+                            hipStream_t stream);
+
+}  // namespace mxfa

@@ -1,0 +1,151 @@
+// quantize.hip -- MXFP8 quantisers for Q/K (rowwise along D) and V (columnwise over 32 tokens plus
+// the token-normalised copy), gfx950.
+//
+// TransformerEngine PR #3865, "Description": P.V contracts over tokens, so V's MXFP8 scale is shared
+// by 32 consecutive tokens of one head-dim column; the own block reads a token-normalised V copy
+// with one power-of-two amplitude per token; Q/K are "rowwise MXFP8 bytes" (blocks of 32 along D).
+// Every block: E8M0 exponent k = least k with amax <= 448 * 2^k, codes = E4M3(x * 2^-k).
+//
+// Both kernels are HBM-bound codecs: one pass over the bf16 input, 16-byte loads, each output
+// written once.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxfa {
+
+// One thread encodes 8 consecutive elements; 4 threads form a 32-element block, 16 a D=128 row.
+__global__ __launch_bounds__(256) void quantize_rowwise_kernel(const uint16_t* __restrict__ x, int S, int H,
+                                                               int64_t sb, int64_t ss, int64_t sh,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales, int64_t nrows) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid >> 4;  // input row order (b, s, h)
+  const int part = (int)(gid & 15);
+  if (row >= nrows) return;  // whole 16-lane rows leave together
+  const int h = (int)(row % H);
+  const int64_t bs = row / H;
+  const int s = (int)(bs % S);
+  const int b = (int)(bs / S);
+  const uint4 raw = *reinterpret_cast<const uint4*>(x + b * sb + s * ss + h * sh + part * 8);
+  float v[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int k = e8m0_exponent(amax);
+  const float m = pow2_neg(k);
+  uint2 out;
+  out.x = pack4_e4m3(v[0] * m, v[1] * m, v[2] * m, v[3] * m);
+  out.y = pack4_e4m3(v[4] * m, v[5] * m, v[6] * m, v[7] * m);
+  const int64_t orow = ((int64_t)b * H + h) * S + s;
+  *reinterpret_cast<uint2*>(codes + orow * 128 + part * 8) = out;
+  if ((part & 3) == 0) scales[orow * 4 + (part >> 2)] = (uint8_t)(k + 127);
+}
+
+// One workgroup per (b, h, group of up to 128 tokens): the bf16 tile is staged in LDS once and read
+// twice, by rows (token-normalised copy) and by columns (columnwise blocks).
+constexpr int VQ_TOK = 128;
+constexpr int VQ_ROW = 128 + 8;  // bf16 elements per LDS row (padding spreads banks)
+
+__global__ __launch_bounds__(256) void quantize_v_kernel(const uint16_t* __restrict__ v, int S, int H, int64_t sb,
+                                                         int64_t ss, int64_t sh, uint8_t* __restrict__ col_codes,
+                                                         uint8_t* __restrict__ col_scales,
+                                                         uint8_t* __restrict__ tn_codes,
+                                                         uint8_t* __restrict__ tn_amps) {
+  __shared__ __align__(16) uint16_t tile[VQ_TOK * VQ_ROW];
+  const int tid = threadIdx.x;
+  const int s0 = blockIdx.x * VQ_TOK, h = blockIdx.y, b = blockIdx.z;
+  const int ntok = min(VQ_TOK, S - s0);  // a multiple of 32
+  const int64_t bh = (int64_t)b * H + h;
+  for (int c = tid; c < ntok * 16; c += 256) {
+    const int r = c >> 4, q = c & 15;
+    const uint4 val = *reinterpret_cast<const uint4*>(v + b * sb + (int64_t)(s0 + r) * ss + h * sh + q * 8);
+    *reinterpret_cast<uint4*>(tile + r * VQ_ROW + q * 8) = val;
+  }
+  __syncthreads();
+
+  // Token-normalised copy: two threads per token, 64 elements each.
+  if (tn_codes) {
+    const int r = tid >> 1, half = tid & 1;
+    if (r < ntok) {
+      const uint16_t* src = tile + r * VQ_ROW + half * 64;
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(src[i])));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      const int k = e8m0_exponent(amax);
+      const float m = pow2_neg(k);
+      uint8_t* dst = tn_codes + (bh * S + s0 + r) * 128 + half * 64;
+#pragma unroll
+      for (int i = 0; i < 64; i += 16) {
+        uint4 o;
+        o.x = pack4_e4m3(bf16_to_f32(src[i + 0]) * m, bf16_to_f32(src[i + 1]) * m, bf16_to_f32(src[i + 2]) * m,
+                         bf16_to_f32(src[i + 3]) * m);
+        o.y = pack4_e4m3(bf16_to_f32(src[i + 4]) * m, bf16_to_f32(src[i + 5]) * m, bf16_to_f32(src[i + 6]) * m,
+                         bf16_to_f32(src[i + 7]) * m);
+        o.z = pack4_e4m3(bf16_to_f32(src[i + 8]) * m, bf16_to_f32(src[i + 9]) * m, bf16_to_f32(src[i + 10]) * m,
+                         bf16_to_f32(src[i + 11]) * m);
+        o.w = pack4_e4m3(bf16_to_f32(src[i + 12]) * m, bf16_to_f32(src[i + 13]) * m, bf16_to_f32(src[i + 14]) * m,
+                         bf16_to_f32(src[i + 15]) * m);
+        *reinterpret_cast<uint4*>(dst + i) = o;
+      }
+      if (half == 0) tn_amps[bh * S + s0 + r] = (uint8_t)(k + 127);
+    }
+  }
+
+  // Columnwise blocks: item = (d, u); four adjacent threads hold the four token blocks of one
+  // column, so together they write 128 contiguous code bytes.
+  if (col_codes) {
+    const int nblk = ntok >> 5;
+    for (int item = tid; item < 128 * 4; item += 256) {
+      const int u = item & 3, d = item >> 2;
+      if (u >= nblk) continue;
+      float x[32];
+      float amax = 0.f;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        x[r] = bf16_to_f32(tile[(32 * u + r) * VQ_ROW + d]);
+        amax = fmaxf(amax, fabsf(x[r]));
+      }
+      const int k = e8m0_exponent(amax);
+      const float m = pow2_neg(k);
+      uint8_t* dst = col_codes + (bh * 128 + d) * S + s0 + 32 * u;
+#pragma unroll
+      for (int r = 0; r < 32; r += 16) {
+        uint4 o;
+        o.x = pack4_e4m3(x[r + 0] * m, x[r + 1] * m, x[r + 2] * m, x[r + 3] * m);
+        o.y = pack4_e4m3(x[r + 4] * m, x[r + 5] * m, x[r + 6] * m, x[r + 7] * m);
+        o.z = pack4_e4m3(x[r + 8] * m, x[r + 9] * m, x[r + 10] * m, x[r + 11] * m);
+        o.w = pack4_e4m3(x[r + 12] * m, x[r + 13] * m, x[r + 14] * m, x[r + 15] * m);
+        *reinterpret_cast<uint4*>(dst + r) = o;
+      }
+      col_scales[(bh * (S / 32) + s0 / 32 + u) * 128 + d] = (uint8_t)(k + 127);
+    }
+  }
+}
+
+hipError_t launch_quantize_rowwise(const uint16_t* x, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t nrows = (int64_t)B * S * H;
+  const int64_t blocks = (nrows * 16 + 255) / 256;
+  quantize_rowwise_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, S, H, sb, ss, sh, codes, scales,
+                                                                             nrows);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_v(const uint16_t* v, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
+                             uint8_t* col_codes, uint8_t* col_scales, uint8_t* tn_codes, uint8_t* tn_amps,
+                             hipStream_t stream) {
+  dim3 grid((unsigned)((S + VQ_TOK - 1) / VQ_TOK), (unsigned)H, (unsigned)B);
+  quantize_v_kernel<<<grid, dim3(256), 0, stream>>>(v, S, H, sb, ss, sh, col_codes, col_scales, tn_codes, tn_amps);
+  return hipGetLastError();
+}
+
+}  // namespace mxfa

@@ -1,0 +1,116 @@
+/*
+ * mxfa.h -- C ABI of libmxfa.so: leak-free causal MXFP8 attention forward for AMD MI355X (gfx950).
+ *
+ * The method is TransformerEngine PR #3865, "[PyTorch] Add causal MXFP8 attention without
+ * future-token leakage through V scales" (section "Description"): a columnwise MXFP8 V scale is
+ * shared by 32 consecutive tokens, so under an ordinary causal mask a later token in a query's own
+ * 32-token block can change how earlier visible V values round. Query i therefore splits its keys at
+ * 32*floor(i/32): completed blocks run in MXFP8 with columnwise V scales that cover visible tokens
+ * only; the query's own block (at most 32 keys) runs on a token-normalised V copy; the two partials
+ * are merged through their log-sum-exps. MXFP8 means E4M3 element codes with one E8M0 power-of-two
+ * scale per 32 elements along the contraction axis (cudnn-frontend PR #1088, PR summary).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller. The library never allocates or
+ *     frees memory, never copies between host and device and never synchronises: all work is
+ *     enqueued on `stream` (a hipStream_t; NULL is the null stream) and runs asynchronously.
+ *   - Every call validates its arguments on the host first. On any error it returns a nonzero
+ *     mxfa_status, enqueues nothing, and mxfa_last_error() names the violated constraint. There is
+ *     no slower fallback path for unsupported shapes.
+ *   - Supported shapes: D == 128, S % 32 == 0, B, S, H >= 1, Hq % Hkv == 0 (GQA: q-head hq reads
+ *     kv-head hq / (Hq/Hkv)), equal query and key lengths, causal.
+ *   - bf16 tensors are addressed by element strides (sb, ss, sh) of a logical [B,S,H,D] tensor with
+ *     unit stride along D (BSHD and SBHD are both such views). Pointers must be 16-byte aligned and
+ *     bf16 strides multiples of 8 elements.
+ *   - Inputs must be finite and the scaled scores finite in fp32; non-finite values are outside the
+ *     contract and are not checked.
+ *   - Code/scale layouts (all row-major, bytes):
+ *       Q/K rowwise codes   [B,H,S,D]      scales [B,H,S,D/32]   (E8M0 bytes, scale = 2^(byte-127))
+ *       V columnwise codes  [B,H,D,S]      scales [B,H,S/32,D]   (keys contiguous per column)
+ *       V token-normalised  [B,H,S,D]      amplitudes [B,H,S]
+ *   - Stateless and thread-safe; calls on one stream run in order.
+ */
+#ifndef MXFA_H
+#define MXFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFA_OK = 0,
+  MXFA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MXFA_ERR_SHAPE = 2,       /* B, S or H out of range, S % 32 != 0, Hq % Hkv != 0, bad view */
+  MXFA_ERR_UNSUPPORTED = 3, /* D != 128, unknown mode or output dtype, workspace too small */
+  MXFA_ERR_ALIGN = 4,       /* pointer not 16-byte aligned or bf16 stride not a multiple of 8 */
+  MXFA_ERR_NO_DEVICE = 5,   /* no HIP device, or the current device is not gfx950 */
+  MXFA_ERR_HIP = 6          /* the HIP runtime reported an error when launching */
+} mxfa_status;
+
+typedef enum { MXFA_QUANT_ROWWISE = 0, MXFA_QUANT_V = 1 } mxfa_quant_mode;
+typedef enum { MXFA_OUT_BF16 = 0, MXFA_OUT_F32 = 1 } mxfa_out_dtype;
+
+/* Text of a status code (static storage). */
+const char* mxfa_status_string(int status);
+/* Detail of the last error returned on this thread ("" if none). */
+const char* mxfa_last_error(void);
+
+/* mxfp8_quantize -- MXFP8 encoding of a bf16 [B,S,H,D] tensor.
+ * Scale rule: the block's E8M0 exponent k is the smallest integer with amax <= 448 * 2^k (no element
+ * saturates; an all-zero block gets byte 0); elements are E4M3 (OCP E4M3FN) codes of x * 2^-k,
+ * rounded to nearest even with the sign of zero kept.
+ *   mode ROWWISE (Q and K; blocks of 32 along D -- "rowwise MXFP8 bytes", TE #3865 Description):
+ *     codes [B,H,S,D], scales [B,H,S,D/32]; tn_codes and tn_amps must be NULL.
+ *   mode V (blocks of 32 consecutive tokens per column -- TE #3865 Description, first paragraph;
+ *     and the token-normalised copy, one power-of-two amplitude per token over all D -- second
+ *     bullet): codes [B,H,D,S], scales [B,H,S/32,D], tn_codes [B,H,S,D], tn_amps [B,H,S].
+ *     Either pair may be NULL to skip that output (not both). */
+int mxfa_mxfp8_quantize(const void* x_bf16, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
+                        int mode, uint8_t* codes, uint8_t* scales, uint8_t* tn_codes, uint8_t* tn_amps,
+                        void* stream);
+
+/* attn_fwd_completed_blocks -- the completed-block partial (TE #3865 Description, first bullet):
+ * for every (b, hq, i), keys j < 32*floor(i/32). Scores t = softmax_scale*log2(e)*(Q^_i . K^_j) come
+ * from block-scaled FP8 products; p = 2^(t - T) with an integer running exponent T; P is quantised
+ * to E4M3 with one E8M0 scale per (query, 32-key block) and multiplied with the columnwise V.
+ * Outputs: o_c fp32 [B,Hq,S,D] = (sum_j p^_j V^_j) / sum_j p_j, lse_c fp32 [B,Hq,S] = natural-log
+ * log-sum-exp of the scaled scores. Rows i < 32 have no completed key: o_c = 0, lse_c = -inf. */
+int mxfa_attn_fwd_completed_blocks(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                   const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D,
+                                   float softmax_scale, float* o_c, float* lse_c, void* stream);
+
+/* attn_fwd_own_block -- the own-block partial (TE #3865 Description, second bullet): for every
+ * (b, hq, i), keys 32*floor(i/32) <= j <= i, softmax in fp32 of softmax_scale * (Q^_i . K^_j) on the
+ * decoded rowwise Q/K, times the decoded token-normalised V. Outputs o_o fp32 [B,Hq,S,D] and
+ * lse_o fp32 [B,Hq,S] (natural log). */
+int mxfa_attn_fwd_own_block(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                            const uint8_t* vt, const uint8_t* vta, int B, int S, int Hq, int Hkv, int D,
+                            float softmax_scale, float* o_o, float* lse_o, void* stream);
+
+/* lse_merge -- merge of the two partials through their log-sum-exps (TE #3865 Description, second
+ * bullet): M = max(lse_c, lse_o), w = e^(lse - M), O = (w_c O_c + w_o O_o) / (w_c + w_o),
+ * lse = M + ln(w_c + w_o). Partials are fp32 [B,H,S,D] / [B,H,S]. The output is written through the
+ * strided view (osb, oss, osh) of a logical [B,S,H,D] tensor as bf16 (round to nearest even) or fp32
+ * per out_dtype; lse_out fp32 [B,H,S] may be NULL. */
+int mxfa_lse_merge(const float* o_c, const float* lse_c, const float* o_o, const float* lse_o, int B, int S, int H,
+                   int D, void* out, int64_t osb, int64_t oss, int64_t osh, int out_dtype, float* lse_out,
+                   void* stream);
+
+/* Bytes of workspace mxfa_attn_fwd needs (codes, scales and fp32 partials, 256-byte aligned parts). */
+size_t mxfa_attn_fwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D);
+
+/* attn_fwd -- the whole forward: the three quantisations, both partials and the merge, in that order
+ * on `stream`, using `workspace` (at least mxfa_attn_fwd_workspace_bytes, 256-byte aligned) for the
+ * intermediates. q [B,S,Hq,D], k and v [B,S,Hkv,D] bf16 views; out is a [B,S,Hq,D] view. */
+int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const void* k, int64_t ksb, int64_t kss,
+                  int64_t ksh, const void* v, int64_t vsb, int64_t vss, int64_t vsh, int B, int S, int Hq, int Hkv,
+                  int D, float softmax_scale, void* workspace, size_t workspace_bytes, void* out, int64_t osb,
+                  int64_t oss, int64_t osh, int out_dtype, float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFA_H */

@@ -27,6 +27,14 @@
  *       full precision (not quantised), V from the token-normalised copy.
  *   R8  A row with no completed key (i < 32) has O_c = 0, lse_c = -inf.
  *   R9  GQA: q-head hq reads kv-head floor(hq / (Hq / Hkv)).
+ *   R15 Several valid results: a kernel forms the scores t in fp32 from a
+ *       hardware block-scaled FP8 dot product whose accumulation is not
+ *       correctly rounded, so a P value lying within that error of an E4M3
+ *       rounding midpoint (or a block maximum within it of an E8M0 step) has
+ *       two valid codes. With `allowance` the completed partial also returns,
+ *       per output element, the largest change any such alternative code can
+ *       make; a score-error bound `score_err` per 64-wide product step (times
+ *       the largest |q.k| product of the step) defines "within".
  */
 #include "oracle.h"
 
@@ -232,15 +240,44 @@ static void quantize_p_block(const double* p, double* phat, int n) {
 
 /* ------------------------------------------------------- partial kernels --- */
 
+/* Bound of the relative error of a kernel's p for key j: the score error bound
+   in log2 units times ln 2, plus fp32 rounding of t - T and of the exponential. */
+static double p_rel_bound(const double* q, const double* k, int D, double sigma, double t, double score_err) {
+  double m0 = 0.0, m1 = 0.0;
+  for (int d = 0; d < D; ++d) {
+    double a = fabs(q[d] * k[d]);
+    if (d < 64) m0 = fmax(m0, a); else m1 = fmax(m1, a);
+  }
+  double dt = sigma * LOG2E * score_err * (m0 + m1) + ldexp(fabs(t) + 1.0, -22);
+  return LN2 * dt + ldexp(1.0, -22);
+}
+
+/* Deterministic jitter in [-1, 1] for (row, key) (splitmix64 of the pair). */
+static double jitter_unit(uint64_t seed, int64_t row, int64_t j) {
+  uint64_t z = seed ^ ((uint64_t)row * 0x9E3779B97F4A7C15ull) ^ ((uint64_t)j * 0xD1B54A32D192ED03ull);
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return (double)(z >> 11) * ldexp(1.0, -52) - 1.0;
+}
+
 /* O7 -- completed-block partial of one query row [TE#3865 Description, first
    bullet: keys j < 32 * floor(i / 32)], or, with `leaky`, the ordinary causal
    MXFP8 row over j <= i. Keys [0, n) with n as above; P blocks are the 32-key
    blocks aligned to multiples of 32 (the last one partial when leaky).
-   quantize_p = 0 replaces the P quantiser by the identity. */
+   quantize_p = 0 replaces the P quantiser by the identity.
+   With `allow` (D values) it also returns the R15 allowance of the row.
+   jitter != 0 moves every score by jitter * (its error bound) * u, u in
+   [-1, 1] from (jitter_seed, row, key): a model of a kernel's score error,
+   used only to pin the allowance. */
 static void completed_row(const double* q, const double* K, const double* V, int i, int D, double sigma,
-                          int quantize_p, int t_shift, int leaky, double* o, double* lse) {
+                          int quantize_p, int t_shift, int leaky, double score_err, double jitter,
+                          uint64_t jitter_seed, int64_t row_id, double* o, double* lse, double* allow) {
   int n = leaky ? i + 1 : 32 * (i / 32);
   for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (allow)
+    for (int d = 0; d < D; ++d) allow[d] = 0.0;
   if (n == 0) { /* R8 */
     *lse = -INFINITY;
     return;
@@ -248,9 +285,13 @@ static void completed_row(const double* q, const double* K, const double* V, int
   double* t = (double*)malloc(sizeof(double) * n);
   double* p = (double*)malloc(sizeof(double) * n);
   double* phat = (double*)malloc(sizeof(double) * n);
+  double* rel = (double*)malloc(sizeof(double) * n);
+  double* alt = (double*)calloc(n, sizeof(double)); /* largest |change| of phat_j over valid codes */
   double tmax = -INFINITY;
   for (int j = 0; j < n; ++j) {
     t[j] = sigma * LOG2E * dot(q, K + (int64_t)j * D, D);
+    if (allow || jitter != 0.0) rel[j] = p_rel_bound(q, K + (int64_t)j * D, D, sigma, t[j], score_err);
+    if (jitter != 0.0) t[j] += jitter * (rel[j] / LN2) * jitter_unit(jitter_seed, row_id, j);
     tmax = fmax(tmax, t[j]);
   }
   double T = ceil(tmax) + t_shift; /* integer exponent offset */
@@ -261,18 +302,46 @@ static void completed_row(const double* q, const double* K, const double* V, int
   }
   for (int u0 = 0; u0 < n; u0 += 32) {
     int m = (n - u0 < 32) ? n - u0 : 32;
-    if (quantize_p)
-      quantize_p_block(p + u0, phat + u0, m);
-    else
+    if (!quantize_p) {
       for (int r = 0; r < m; ++r) phat[u0 + r] = p[u0 + r];
+      continue;
+    }
+    quantize_p_block(p + u0, phat + u0, m);
+    if (!allow) continue;
+    /* R15: element codes within the bound of a midpoint, and block scales
+       within the bound of an E8M0 step, each give an alternative value. */
+    double amax = 0.0, rmax = 0.0;
+    for (int r = 0; r < m; ++r) {
+      amax = fmax(amax, (double)(float)p[u0 + r]);
+      rmax = fmax(rmax, rel[u0 + r]);
+    }
+    int klo = orc_e8m0_exponent(amax * (1.0 - rmax)), khi = orc_e8m0_exponent(amax * (1.0 + rmax));
+    for (int r = 0; r < m; ++r) {
+      double y = (double)(float)p[u0 + r];
+      for (int kk = klo; kk <= khi; ++kk) {
+        double lo = ldexp(orc_e4m3_decode(orc_e4m3_encode(ldexp(y * (1.0 - rel[u0 + r]), -kk))), kk);
+        double hi = ldexp(orc_e4m3_decode(orc_e4m3_encode(ldexp(y * (1.0 + rel[u0 + r]), -kk))), kk);
+        double ch = fmax(fabs(lo - phat[u0 + r]), fabs(hi - phat[u0 + r]));
+        /* values between lo and hi map to codes between them: lo and hi bound the change */
+        alt[u0 + r] = fmax(alt[u0 + r], ch);
+      }
+    }
   }
   for (int j = 0; j < n; ++j)
     for (int d = 0; d < D; ++d) o[d] += phat[j] * V[(int64_t)j * D + d];
   for (int d = 0; d < D; ++d) o[d] /= l;
+  if (allow) {
+    for (int j = 0; j < n; ++j)
+      if (alt[j] > 0.0)
+        for (int d = 0; d < D; ++d) allow[d] += alt[j] * fabs(V[(int64_t)j * D + d]);
+    for (int d = 0; d < D; ++d) allow[d] /= l;
+  }
   *lse = LN2 * (T + log2(l));
   free(t);
   free(p);
   free(phat);
+  free(rel);
+  free(alt);
 }
 
 /* O8 -- own-block partial of one query row [TE#3865 Description, second
@@ -324,8 +393,8 @@ static int row_index(const int32_t* rows, int r) { return rows ? rows[r] : r; }
 /* Runs one partial over every (b, hq, listed row). Q, K, V are decoded
    token-major [B,H,S,D] tensors. */
 static void run_rows(int part, const double* Q, const double* K, const double* V, int B, int S, int Hq, int Hkv,
-                     int D, float scale, const int32_t* rows, int nrows, int quantize_p, int t_shift, double* o,
-                     double* lse) {
+                     int D, float scale, const int32_t* rows, int nrows, int quantize_p, int t_shift,
+                     double score_err, double jitter, uint64_t jitter_seed, double* o, double* lse, double* allow) {
   assert(Hq % Hkv == 0);
   const int G = Hq / Hkv;
   const double sigma = (double)scale;
@@ -360,18 +429,22 @@ static void run_rows(int part, const double* Q, const double* K, const double* V
           lse[orow] = m + log(l);
           free(s);
         } else {
-          completed_row(q, Kh, Vh, i, D, sigma, quantize_p, t_shift, part == PART_LEAKY, o + orow * D, lse + orow);
+          completed_row(q, Kh, Vh, i, D, sigma, quantize_p, t_shift, part == PART_LEAKY, score_err, jitter,
+                        jitter_seed, ((int64_t)b * Hq + hq) * S + i, o + orow * D, lse + orow,
+                        allow ? allow + orow * D : NULL);
         }
       }
 }
 
 void orc_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                         const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale,
-                        const int32_t* rows, int nrows, int t_shift, double* o, double* lse) {
+                        const int32_t* rows, int nrows, int t_shift, double* o, double* lse, double score_err,
+                        double* allowance, double jitter, uint64_t jitter_seed) {
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vcol(vc, vcs, B, Hkv, S, D);
-  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, t_shift, o, lse);
+  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, t_shift, score_err, jitter,
+           jitter_seed, o, lse, allowance);
   free(Q);
   free(K);
   free(V);
@@ -383,7 +456,7 @@ void orc_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vcol(vc, vcs, B, Hkv, S, D);
-  run_rows(PART_LEAKY, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, 0, o, lse);
+  run_rows(PART_LEAKY, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, 0, 0.0, 0.0, 0, o, lse, NULL);
   free(Q);
   free(K);
   free(V);
@@ -395,7 +468,7 @@ void orc_attn_own(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vtn(vt, vta, B, Hkv, S, D);
-  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, o, lse);
+  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, o, lse, NULL);
   free(Q);
   free(K);
   free(V);
@@ -408,7 +481,7 @@ void orc_attn_reference(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh
   double* Q = bf16_tensor(q, qsb, qss, qsh, B, S, Hq, D);
   double* K = bf16_tensor(k, ksb, kss, ksh, B, S, Hkv, D);
   double* V = bf16_tensor(v, vsb, vss, vsh, B, S, Hkv, D);
-  run_rows(PART_TEXTBOOK, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, o, lse);
+  run_rows(PART_TEXTBOOK, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, o, lse, NULL);
   free(Q);
   free(K);
   free(V);
@@ -426,8 +499,8 @@ void orc_attn_identity(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh,
   double* oo = (double*)malloc(sizeof(double) * n * D);
   double* lc = (double*)malloc(sizeof(double) * n);
   double* lo = (double*)malloc(sizeof(double) * n);
-  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, oc, lc);
-  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, oo, lo);
+  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, oc, lc, NULL);
+  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, oo, lo, NULL);
   orc_lse_merge(oc, lc, oo, lo, n, D, o, lse);
   free(oc);
   free(oo);

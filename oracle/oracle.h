@@ -51,10 +51,16 @@ void orc_quantize_v(const uint16_t* v, int B, int S, int H, int D, int64_t sb, i
                     uint8_t* col_codes, uint8_t* col_scales, uint8_t* tn_codes, uint8_t* tn_amps);
 
 /* O7: completed-block partial. t_shift adds an integer to the running
-   exponent T (any integer gives the same result; used as a pin). */
+   exponent T (any integer gives the same result; used as a pin).
+   allowance (may be NULL, else [B,Hq,nrows,D]): per element, the largest
+   change of O_c that alternative valid P codes can make when a kernel's score
+   error is bounded by score_err * (largest |q.k| product of each 64-wide step)
+   in log2 units (reading R15). jitter/jitter_seed: if jitter != 0, every score
+   is moved by jitter * its bound * u, u in [-1, 1] (test model of a kernel). */
 void orc_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                         const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale,
-                        const int32_t* rows, int nrows, int t_shift, double* o, double* lse);
+                        const int32_t* rows, int nrows, int t_shift, double* o, double* lse, double score_err,
+                        double* allowance, double jitter, uint64_t jitter_seed);
 /* O8: own-block partial on the token-normalised V. */
 void orc_attn_own(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
                   const uint8_t* vta, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,

@@ -1,0 +1,85 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the HIP path through the
+C ABI binding, sample rows, and compare against the oracle with a report of the worst elements."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import causal_mxfp8_block_amd as mx
+import oracle
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def oracle_view(inp, name):
+    x = getattr(inp, name)
+    return oracle.BF16View.sbhd(x) if inp.workload.layout == "sbhd" else oracle.BF16View.bshd(x)
+
+
+def gpu_quantize(inp):
+    lay = inp.workload.layout
+    q, k, v = (to_dev(getattr(inp, n)) for n in ("q", "k", "v"))
+    qc, qs = mx.mxfp8_quantize(q, "rowwise", lay)
+    kc, ks = mx.mxfp8_quantize(k, "rowwise", lay)
+    vc, vcs, vt, vta = mx.mxfp8_quantize(v, "v", lay)
+    return dict(qc=qc, qs=qs, kc=kc, ks=ks, vc=vc, vcs=vcs, vt=vt, vta=vta)
+
+
+def gpu_forward(inp, out_dtype=torch.float32):
+    """Whole forward through mxfa_attn_fwd; returns (O [B,Hq,S,D] float64 numpy, lse [B,Hq,S])."""
+    lay = inp.workload.layout
+    q, k, v = (to_dev(getattr(inp, n)) for n in ("q", "k", "v"))
+    out, lse = mx.attn_fwd(q, k, v, inp.workload.scale, layout=lay, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o = out.float()
+    o = o.permute(0, 2, 1, 3) if lay == "bshd" else o.permute(1, 2, 0, 3)
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def sample_rows(S: int, seed: int, n_random: int = 192, head: int = 96, tail: int = 32, stride: int = 1024):
+    """Rows 0..head-1, every stride-th row, the last `tail` rows and n_random seeded uniform rows."""
+    rng = np.random.default_rng(seed + 1000)
+    rows = set(range(min(head, S))) | set(range(0, S, stride)) | set(range(max(0, S - tail), S))
+    rows |= set(rng.integers(0, S, size=n_random).tolist())
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+def uniform_rows(S: int, seed: int, n: int = 256):
+    rng = np.random.default_rng(seed + 2000)
+    return np.unique(rng.integers(0, S, size=n)).astype(np.int32)
+
+
+def report(name, got, ref, rms, rows=None, allowance=None, tol=None, k=5):
+    """Prints the comparison and returns max(|err| - allowance) / rms (the gated figure).
+
+    ``allowance`` (oracle reading R15) is the largest change that alternative valid P codes can
+    make per element; without it the gated figure is max|err| / rms."""
+    err = np.abs(got - ref)
+    al = np.zeros_like(err) if allowance is None else allowance
+    excess = err - al
+    gated = excess.max() / rms
+    msg = (f"[{name}] max|err|/rms = {err.max() / rms:.3e}  rms(err)/rms = {np.sqrt(np.mean(err ** 2)) / rms:.3e}"
+           f"  rms(ref) = {rms:.3e}")
+    if allowance is not None:
+        msg += f"  max(|err|-allow)/rms = {gated:.3e}  mean(allow)/rms = {al.mean() / rms:.2e}"
+        if tol is not None:
+            msg += f"  elements over tol without allowance: {int(np.sum(err > tol * rms))} of {err.size}"
+    say(msg)
+    worst = np.argsort(excess.reshape(-1))[::-1][:k]
+    for w in worst:
+        idx = np.unravel_index(w, err.shape)
+        row = rows[idx[2]] if rows is not None and len(idx) > 2 else (idx[2] if len(idx) > 2 else None)
+        say(f"    at (b, h, row, d) = ({idx[0]}, {idx[1]}, {row}, {idx[-1] if len(idx) > 3 else '-'}): "
+            f"got {got[idx]:.6e} ref {ref[idx]:.6e} allowance {al[idx]:.3e}")
+    return gated

@@ -1,0 +1,100 @@
+"""Host-side checks of the C ABI (no GPU needed): libmxfa.so loads, exports every entry point that
+include/mxfa.h declares, and rejects invalid arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_mxfp8_block_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["mxfa_mxfp8_quantize", "mxfa_attn_fwd_completed_blocks", "mxfa_attn_fwd_own_block",
+              "mxfa_lse_merge", "mxfa_attn_fwd", "mxfa_attn_fwd_workspace_bytes", "mxfa_status_string",
+              "mxfa_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mx.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_exports_nothing_undeclared():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mx.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l and l.split()[-1].startswith("mxfa")}
+    assert exported == set(declared_functions())
+
+
+def _err(status):
+    return status, mx.lib().mxfa_last_error().decode()
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(D=64), 3, "D = 64"),
+    (dict(S=48), 2, "multiple of 32"),
+    (dict(Hq=6, Hkv=4), 2, "multiple of Hkv"),
+    (dict(B=0), 2, ">= 1"),
+    (dict(qc=None), 1, "qc is NULL"),
+    (dict(vcs=FAKE + 4), 4, "vcs is not 16-byte aligned"),
+])
+def test_completed_validation(args, status, needle):
+    a = dict(qc=FAKE, qs=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vcs=FAKE, B=1, S=64, Hq=4, Hkv=2, D=128)
+    a.update(args)
+    st, msg = _err(mx.lib().mxfa_attn_fwd_completed_blocks(a["qc"], a["qs"], a["kc"], a["ks"], a["vc"], a["vcs"],
+                                                           a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], 0.1, FAKE,
+                                                           FAKE, None))
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_quantize_validation():
+    L = mx.lib()
+    st, msg = _err(L.mxfa_mxfp8_quantize(FAKE, 1, 64, 2, 128, 64 * 256, 256, 128, 7, FAKE, FAKE, None, None, None))
+    assert st == 3 and "mode" in msg
+    st, msg = _err(L.mxfa_mxfp8_quantize(FAKE, 1, 64, 2, 128, 64 * 256, 256, 12, 0, FAKE, FAKE, None, None, None))
+    assert st in (2, 4)
+    st, msg = _err(L.mxfa_mxfp8_quantize(FAKE, 1, 64, 2, 128, 64 * 256, 256, 128, 0, FAKE, FAKE, FAKE, FAKE, None))
+    assert st == 3 and "token-normalised" in msg
+    st, msg = _err(L.mxfa_mxfp8_quantize(FAKE, 1, 40, 2, 128, 40 * 256, 256, 128, 1, FAKE, FAKE, None, None, None))
+    assert st == 2
+
+
+def test_merge_and_forward_validation():
+    L = mx.lib()
+    st, msg = _err(L.mxfa_lse_merge(FAKE, FAKE, FAKE, FAKE, 1, 64, 2, 128, FAKE, 64 * 256, 256, 128, 5, None, None))
+    assert st == 3
+    need = L.mxfa_attn_fwd_workspace_bytes(1, 64, 4, 2, 128)
+    assert need > 0
+    st, msg = _err(L.mxfa_attn_fwd(FAKE, 64 * 512, 512, 128, FAKE, 64 * 256, 256, 128, FAKE, 64 * 256, 256, 128,
+                                   1, 64, 4, 2, 128, 0.1, FAKE, need - 1, FAKE, 64 * 512, 512, 128, 0, None, None))
+    assert st == 3 and "workspace" in msg
+    st, msg = _err(L.mxfa_attn_fwd(FAKE, 64 * 512, 512, 128, FAKE, 64 * 256, 256, 128, FAKE, 64 * 256, 256, 128,
+                                   1, 64, 4, 2, 128, 0.1, FAKE + 256 * 3 + 16, need, FAKE, 64 * 512, 512, 128, 0,
+                                   None, None))
+    assert st == 4
+
+
+def test_no_device_is_an_error_not_a_crash():
+    """Valid arguments on a machine without a gfx950 device return MXFA_ERR_NO_DEVICE."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, msg = _err(mx.lib().mxfa_attn_fwd_completed_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 128,
+                                                           0.1, FAKE, FAKE, None))
+    assert st == 5, msg

@@ -170,3 +170,36 @@ def test_leaky_differs_from_leak_free_only_inside_blocks():
     ref, _ = bf.textbook_attention(inp.q, inp.k, inp.v, SCALE)
     rms = np.sqrt(np.mean(ref ** 2))
     assert np.max(np.abs(o - ref)) < 0.2 * rms * 10 and np.max(np.abs(ol - ref)) < 0.2 * rms * 10
+
+
+@pytest.mark.parametrize("values,jitter", [("normal", 1.0), ("outliers", 1.0), ("token_amplitudes", 0.5)])
+def test_allowance_covers_score_error(values, jitter):
+    """R15 pin: moving every score by up to its error bound (a model of the hardware dot product)
+    changes the completed partial by at most the allowance, plus the change of the normaliser
+    l = sum p (at most the largest relative error of p, times |O_c|)."""
+    inp = _inputs(S=512, Hq=4, Hkv=2, seed=17, values=values)
+    z = oracle.quantize_all(inp.q, inp.k, inp.v)
+    o0, l0, al = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 4, 2, SCALE, allowance=True)
+    flips_seen = 0
+    for seed in range(3):
+        o1, _ = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 4, 2, SCALE, jitter=jitter,
+                                      jitter_seed=seed)
+        slack = 2e-3 * np.abs(o0) + 1e-12  # l moves by < 1e-3 relative at this bound
+        excess = np.abs(o1 - o0) - al - slack
+        assert excess.max() <= 0, excess.max()
+        flips_seen += int(np.sum(np.abs(o1 - o0) > slack))
+    assert flips_seen > 0  # the jitter did flip codes, so the bound was exercised
+    # and the allowance stays small next to the outputs
+    rms = np.sqrt(np.mean(o0[:, :, 32:] ** 2))
+    assert np.mean(al[:, :, 32:]) < 0.05 * rms
+
+
+def test_allowance_vanishes_without_score_error():
+    """With a zero score-error bound only fp32-rounding-sized windows remain: almost no key is
+    ambiguous."""
+    inp = _inputs(S=256, Hq=2, Hkv=1, seed=18)
+    z = oracle.quantize_all(inp.q, inp.k, inp.v)
+    _, _, al = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 2, 1, SCALE, allowance=True, score_err=0.0)
+    _, _, al2 = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 2, 1, SCALE, allowance=True)
+    assert np.mean(al > 0) < 0.2 * max(np.mean(al2 > 0), 1e-9) + 0.02
+    assert al.sum() <= al2.sum()
