@@ -1,0 +1,219 @@
+"""Benchmark: leak-free causal MXFP8 attention forward on one MI355X.
+
+One step is one pass of the whole forward path over one batch: MXFP8 quantisation of Q, K (rowwise)
+and V (columnwise + token-normalised), the completed-block partial, the own-block partial and the
+LSE merge (bf16 output), each through the C ABI of libmxfa.so on torch's current stream. Inputs are
+seeded synthetic bf16 tensors already resident in HBM when the timed region starts.
+
+Workload (the configuration the published forward timings are quoted on): B=1, 16 query heads,
+4 KV heads, S=32768, D=128, BSHD, causal, V rows scaled by 2^e, e ~ U{-4..4} per (token, kv-head).
+
+Prints one JSON line. `value` is TFLOP/s of the whole forward with the FlashAttention causal count
+2*B*Hq*S^2*D; `roofline` is the completed-block kernel (the dominant one) against the MXFP8 MFMA
+peak, from HIP events around its launches in the timed steps; `cpu_baseline` times the fp64 CPU
+oracle on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal MXFP8 attn fwd TFLOP/s + ms at B=1,H=16/4,S=32K,D=128; % MFMA peak"
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8/MXFP8 MFMA
+HBM_PEAK_GBS = 8000.0
+# Published own-block forward time for this workload (B200, includes quantisation): 2.797 ms,
+# i.e. 2*1*16*32768^2*128 / 2.797 ms = 1572.4 TFLOP/s. Context from other hardware, not a target.
+PAGES_TFLOPS = 2 * 16 * 32768 ** 2 * 128 / 2.797e-3 / 1e12
+
+
+def completed_pairs(B, Hq, S):
+    n = S // 32
+    return B * Hq * 1024 * (n * (n - 1) // 2)  # sum_i 32*floor(i/32) over i < S
+
+
+def own_pairs(B, Hq, S):
+    return B * Hq * (S // 32) * (32 * 33 // 2)
+
+
+def read_traffic(kernel_source: str):
+    """HBM traffic of the completed-block kernel per launch from the committed PMC summary, or None
+    when the summary is missing or was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "completed_kernel_gqa16x4_s32k_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = hashlib.sha256(open(kernel_source, "rb").read()).hexdigest()[:16]
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != sha:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(inp, rows_n: int, seed: int = 0):
+    """The oracle as it stands on a row sample of the same workload (quantisation of the whole
+    tensors included); TFLOP/s counts 4*D per (query, visible key) pair of the sampled rows."""
+    import oracle
+    w = inp.workload
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(w.S, size=rows_n, replace=False)).astype(np.int32)
+    view = oracle.BF16View.sbhd if w.layout == "sbhd" else oracle.BF16View.bshd
+    q, k, v = view(inp.q), view(inp.k), view(inp.v)
+    oracle.build()
+    t0 = time.perf_counter()
+    z = oracle.quantize_all(q, k, v)
+    oc, lc = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale, rows)
+    oo, lo = oracle.attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, w.Hq, w.Hkv, w.scale, rows)
+    oracle.lse_merge(oc, lc, oo, lo)
+    dt = time.perf_counter() - t0
+    flops = float(np.sum(4.0 * w.D * (rows.astype(np.float64) + 1)) * w.B * w.Hq)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = min(cores, os.cpu_count() or cores)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows_n} seeded random query rows x {w.Hq} heads of {w.name} (all keys of each row), "
+                      f"plus quantisation of the whole Q/K/V; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa16x4_s32k_amplitudes")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle CPU-baseline sample (0 skips)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_mxfp8_block_amd as mx
+    from causal_mxfp8_block_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = to(inp.q), to(inp.k), to(inp.v)
+    lay = w.layout
+    B, S, Hq, Hkv, D = w.B, w.S, w.Hq, w.Hkv, w.D
+    u8, f32 = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.float32, device=dev)
+    qc, qs = torch.empty((B, Hq, S, D), **u8), torch.empty((B, Hq, S, D // 32), **u8)
+    kc, ks = torch.empty((B, Hkv, S, D), **u8), torch.empty((B, Hkv, S, D // 32), **u8)
+    vc, vcs = torch.empty((B, Hkv, D, S), **u8), torch.empty((B, Hkv, S // 32, D), **u8)
+    vt, vta = torch.empty((B, Hkv, S, D), **u8), torch.empty((B, Hkv, S), **u8)
+    oc, lc = torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)
+    oo, lo = torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, S), **f32)
+    L = mx.lib()
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    names = ["quantize_q", "quantize_k", "quantize_v", "completed", "own_block", "merge"]
+
+    def view(t):
+        return mx.view_of(t, lay)
+
+    qv, kv_, vv, ov = view(q), view(k), view(v), view(out)
+
+    def step(evs=None):
+        calls = [
+            lambda: L.mxfa_mxfp8_quantize(q.data_ptr(), B, S, Hq, D, *qv[4:], mx.ROWWISE, qc.data_ptr(),
+                                          qs.data_ptr(), None, None, sh),
+            lambda: L.mxfa_mxfp8_quantize(k.data_ptr(), B, S, Hkv, D, *kv_[4:], mx.ROWWISE, kc.data_ptr(),
+                                          ks.data_ptr(), None, None, sh),
+            lambda: L.mxfa_mxfp8_quantize(v.data_ptr(), B, S, Hkv, D, *vv[4:], mx.V, vc.data_ptr(), vcs.data_ptr(),
+                                          vt.data_ptr(), vta.data_ptr(), sh),
+            lambda: L.mxfa_attn_fwd_completed_blocks(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                                     vc.data_ptr(), vcs.data_ptr(), B, S, Hq, Hkv, D, w.scale,
+                                                     oc.data_ptr(), lc.data_ptr(), sh),
+            lambda: L.mxfa_attn_fwd_own_block(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                              vt.data_ptr(), vta.data_ptr(), B, S, Hq, Hkv, D, w.scale,
+                                              oo.data_ptr(), lo.data_ptr(), sh),
+            lambda: L.mxfa_lse_merge(oc.data_ptr(), lc.data_ptr(), oo.data_ptr(), lo.data_ptr(), B, S, Hq, D,
+                                     out.data_ptr(), *ov[4:], mx.OUT_BF16, lse.data_ptr(), sh),
+        ]
+        for i, c in enumerate(calls):
+            if evs is not None:
+                evs[i][0].record(stream)
+            st = c()
+            if st != 0:
+                raise mx.MxfaError(st, L.mxfa_last_error().decode())
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per = {n: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+
+    flops = 2.0 * B * Hq * S * S * D
+    comp_flops = 512.0 * completed_pairs(B, Hq, S)
+    own_flops = 512.0 * own_pairs(B, Hq, S)
+    achieved = comp_flops / (per["completed"] * 1e-3) / 1e12
+    n_q, n_kv = B * Hq * S, B * Hkv * S
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    kernels = {
+        "quantize_q": {"ms": per["quantize_q"], "GB/s": gbs(n_q * D * (2 + 1 + 1 / 32), per["quantize_q"])},
+        "quantize_k": {"ms": per["quantize_k"], "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32), per["quantize_k"])},
+        "quantize_v": {"ms": per["quantize_v"],
+                       "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32 + 1 + 1 / 128), per["quantize_v"])},
+        "completed": {"ms": per["completed"], "TFLOP/s": achieved, "algorithmic_flop": comp_flops},
+        "own_block": {"ms": per["own_block"], "TFLOP/s": own_flops / (per["own_block"] * 1e-3) / 1e12,
+                      "GB/s": gbs(n_q * (D + 4 + D * 4 + 4) + n_kv * 2 * (D + 4), per["own_block"])},
+        "merge": {"ms": per["merge"], "GB/s": gbs(n_q * (2 * D * 4 + 2 * 4 + D * 2 + 4), per["merge"])},
+    }
+    src = os.path.join(ROOT, "causal_mxfp8_block_amd", "csrc", "attn_completed.hip")
+    traffic = read_traffic(src)
+    value = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_TFLOPS, 4),
+        "dtype": "mxfp8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "layout": lay,
+                   "causal": True, "values": w.values, "output": "bf16"},
+        "pct_mfma_peak": round(100.0 * value / MFMA_FP8_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "completed_kernel", "launch_ms": round(per["completed"], 4)},
+        "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in d.items()}
+                    for n, d in kernels.items()},
+        "cpu_baseline": None,
+    }
+    if args.cpu_rows > 0:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
