@@ -18,7 +18,12 @@
 //    v_cvt_scalef32_pk_fp8_f32; four v_permlane32_swaps move the codes into the B-operand layout of
 //    O^T = V^T . P^T (block-scaled FP8 MFMA again, V columnwise codes keys-contiguous per column).
 //  * O^T leaves one query per lane too, so the rescale and the final 1/l are per-lane scalars.
-//  * K and V tiles of 64 keys are staged in LDS once per workgroup and shared by the 4 waves.
+//  * K and V tiles of 64 keys are staged in LDS once per workgroup and shared by the 4 waves; the
+//    LDS is double-buffered and the next tile's global loads are in flight while the current tile
+//    computes, so one barrier per tile remains.
+//  * Two workgroups per CU (two waves per SIMD) so one wave's softmax overlaps another's MFMAs.
+//  * Full tiles and the half tile at the end of a wave's range are separate code paths, so the
+//    common path has no per-element select.
 //  * Workgroups are launched longest-first (the causal work of a query tile grows with its index).
 #include "device_common.h"
 #include "launch.h"
@@ -31,7 +36,7 @@ constexpr int CB_KROW = 144;  // LDS bytes per K row (128 codes + 16 pad: confli
 constexpr int CB_VROW = 80;   // LDS bytes per V column (64 codes + 16 pad)
 constexpr float CB_PMAX_LAZY = 256.0f;  // raise T once a block maximum of p exceeds 2^8
 
-struct __align__(16) CompletedSmem {
+struct __align__(16) TileSmem {
   uint8_t k[CB_BN * CB_KROW];  // K codes, key-major
   uint8_t v[128 * CB_VROW];    // V codes, column-major (keys contiguous)
   uint32_t ks[CB_BN];          // the 4 E8M0 bytes of each key
@@ -45,21 +50,166 @@ __device__ __forceinline__ v8i make_v8i(uint4 a, uint4 b) {
   return r;
 }
 
-// Exchange with lane ^ 32: returns (x of lanes 0..31, y of lanes 32..63) arranged as the builtin
-// does: after swap(x, y), x in lanes 32..63 and y in lanes 0..31 have traded places.
+// Exchange with lane ^ 32 (v_permlane32_swap): afterwards x holds, in lanes 32..63, what y held in
+// lanes 0..31, and y holds, in lanes 0..31, what x held in lanes 32..63.
 __device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
   auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
   x = r[0];
   y = r[1];
 }
+__device__ __forceinline__ void swap32f(float& x, float& y) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = __builtin_bit_cast(uint32_t, y);
+  swap32(a, b);
+  x = __builtin_bit_cast(float, a);
+  y = __builtin_bit_cast(float, b);
+}
 
-__global__ __launch_bounds__(256) void completed_kernel(const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs,
-                                                        const uint8_t* __restrict__ kc, const uint8_t* __restrict__ ks,
-                                                        const uint8_t* __restrict__ vc,
-                                                        const uint8_t* __restrict__ vcs, int S, int Hq, int Hkv,
-                                                        float scale_log2, float* __restrict__ o_c,
-                                                        float* __restrict__ lse_c, int n_qtiles) {
-  __shared__ CompletedSmem sm;
+// One thread's share of a tile load: two 16-byte K chunks, two 16-byte V chunks and, for threads
+// 0..127, one word of scales. Threads 0..63 fetch the 4 scale bytes of key tid, threads 64..127 one
+// word of the two V scale blocks.
+#define TILE_LOAD(k0, k1, v0, v1, sc, kt0)                                                            \
+  do {                                                                                                \
+    const uint8_t* ksrc_ = kc + (bhk * S + (kt0) + (tid >> 2)) * 128 + (tid & 3) * 32;                \
+    k0 = *reinterpret_cast<const uint4*>(ksrc_);                                                     \
+    k1 = *reinterpret_cast<const uint4*>(ksrc_ + 16);                                                \
+    const uint8_t* vsrc_ = vc + (bhk * 128 + (tid >> 1)) * S + (kt0) + (tid & 1) * 32;               \
+    v0 = *reinterpret_cast<const uint4*>(vsrc_);                                                     \
+    v1 = *reinterpret_cast<const uint4*>(vsrc_ + 16);                                                \
+    sc = (tid < 64) ? *reinterpret_cast<const uint32_t*>(ks + (bhk * S + (kt0) + (tid & 63)) * 4)    \
+                    : *reinterpret_cast<const uint32_t*>(vcs + (bhk * (S / 32) + (kt0) / 32) * 128 + \
+                                                         (tid & 63) * 4);                            \
+  } while (0)
+
+__device__ __forceinline__ void store_tile(TileSmem& t, uint4 k0, uint4 k1, uint4 v0, uint4 v1, uint32_t sc,
+                                           int tid) {
+  const int kr = tid >> 2, kch = (tid & 3) * 32;
+  *reinterpret_cast<uint4*>(t.k + kr * CB_KROW + kch) = k0;
+  *reinterpret_cast<uint4*>(t.k + kr * CB_KROW + kch + 16) = k1;
+  const int d = tid >> 1, hv = (tid & 1) * 32;
+  *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv) = v0;
+  *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv + 16) = v1;
+  if (tid < 64)
+    t.ks[tid] = sc;
+  else if (tid < 128)
+    *reinterpret_cast<uint32_t*>(t.vs + (tid - 64) * 4) = sc;
+}
+
+// Per-wave running state of the online softmax.
+struct RowState {
+  v16f o[4];   // O^T accumulator: lane (c, hf), element i of tile dt -> column 32dt + 8(i/4) + 4hf + i%4
+  float T;     // integer-valued running exponent
+  float lsum;  // this lane's share of sum p
+};
+
+// One 64-key tile for one wave. kFull: both 32-key blocks are completed keys of this wave; otherwise
+// only the first block is (the second one's p is zero and its MFMA is skipped).
+template <bool kFull>
+__device__ __forceinline__ void process_tile(RowState& st, const TileSmem& t, const v8i (&qop)[2],
+                                             const int (&qsc)[2], float scale_log2, int c, int hf) {
+  // ---- S^T = K Q^T for the tile's 32-key blocks --------------------------------------------
+  v16f sacc[2];
+#pragma unroll
+  for (int kt = 0; kt < (kFull ? 2 : 1); ++kt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+    const uint32_t ksw = t.ks[32 * kt + c];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t* kr = t.k + (32 * kt + c) * CB_KROW + 64 * m + 16 * hf;
+      const v8i kop = make_v8i(*reinterpret_cast<const uint4*>(kr), *reinterpret_cast<const uint4*>(kr + 32));
+      const int ksc = (int)((ksw >> (8 * (2 * m + hf))) & 0xffu);
+      sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[m], sacc[kt], 0, 0, 0, ksc, 0, qsc[m]);
+    }
+  }
+  // Lane (c, hf), element i of block kt holds key 32kt + 8(i/4) + 4hf + (i%4) of the tile, query c.
+
+  // ---- p = 2^(t - T) and the two block maxima ------------------------------------------------
+  float p[2][16];
+  float M0, M1;
+  for (int pass = 0; pass < 2; ++pass) {
+    const float negT = -st.T;
+    float pm0 = 0.f, pm1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[0][i] = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], scale_log2, negT));
+      pm0 = fmaxf(pm0, p[0][i]);
+      if (kFull) {
+        p[1][i] = __builtin_amdgcn_exp2f(fmaf(sacc[1][i], scale_log2, negT));
+        pm1 = fmaxf(pm1, p[1][i]);
+      } else {
+        p[1][i] = 0.f;
+      }
+    }
+    swap32f(pm0, pm1);  // lanes 0..31 now see both halves of block 0, lanes 32..63 of block 1
+    float mo = fmaxf(pm0, pm1), mo2 = mo;
+    swap32f(mo, mo2);  // every lane: mo = block-0 maximum, mo2 = block-1 maximum
+    M0 = mo;
+    M1 = mo2;
+    if (!__any(fmaxf(M0, M1) > CB_PMAX_LAZY)) break;
+    // Rare path: raise T to ceil(row max of t) and rescale by the exact power of two 2^(T - Tn).
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mt = fmaxf(mt, sacc[0][i] * scale_log2);
+      if (kFull) mt = fmaxf(mt, sacc[1][i] * scale_log2);
+    }
+    float mt2 = mt;
+    swap32f(mt, mt2);
+    mt = fmaxf(mt, mt2);
+    const float Tn = fmaxf(st.T, ceilf(mt));
+    const float f = __builtin_amdgcn_exp2f(st.T - Tn);  // 0 on the first tile, else 2^-(integer)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[dt][i] *= f;
+    st.lsum *= f;
+    st.T = Tn;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.lsum += kFull ? p[0][i] + p[1][i] : p[0][i];
+
+  // ---- quantise P: one E8M0 per (query, 32-key block) --------------------------------------
+  // Exponent -127 is only reached by blocks whose largest p is below 2^-118; they use -126 so the
+  // conversion's power-of-two divisor stays a normal fp32 value.
+  const int k0 = max(e8m0_exponent(M0), -126), k1 = max(e8m0_exponent(M1), -126);
+  const float sc0 = u2f((uint32_t)(127 + k0) << 23), sc1 = u2f((uint32_t)(127 + k1) << 23);
+  uint32_t sl[8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    sl[g] = pack4_e4m3_scaled(p[0][4 * g], p[0][4 * g + 1], p[0][4 * g + 2], p[0][4 * g + 3], sc0);
+    sl[4 + g] = kFull ? pack4_e4m3_scaled(p[1][4 * g], p[1][4 * g + 1], p[1][4 * g + 2], p[1][4 * g + 3], sc1) : 0u;
+  }
+  // Slot g holds keys 8g + 4hf + [0,4) of its block. The B operand of O^T wants, in lane hf,
+  // keys 16hf + [0,16) of block 0 then of block 1: trade slots 2,3 (6,7) of the lower half for
+  // slots 0,1 (4,5) of the upper half.
+  swap32(sl[0], sl[2]);
+  swap32(sl[1], sl[3]);
+  swap32(sl[4], sl[6]);
+  swap32(sl[5], sl[7]);
+  v8i pop;
+  pop[0] = (int)sl[0]; pop[1] = (int)sl[2]; pop[2] = (int)sl[1]; pop[3] = (int)sl[3];
+  pop[4] = (int)sl[4]; pop[5] = (int)sl[6]; pop[6] = (int)sl[5]; pop[7] = (int)sl[7];
+  const int psc = (hf ? k1 : k0) + 127;
+
+  // ---- O^T += V^T P^T over the four 32-column tiles of D -----------------------------------
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const uint8_t* vr = t.v + (32 * dt + c) * CB_VROW + 16 * hf;
+    const v8i vop = make_v8i(*reinterpret_cast<const uint4*>(vr), *reinterpret_cast<const uint4*>(vr + 32));
+    const int vsc = t.vs[hf * 128 + 32 * dt + c];
+    st.o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, st.o[dt], 0, 0, 0, vsc, 0, psc);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void completed_kernel(const uint8_t* __restrict__ qc,
+                                                           const uint8_t* __restrict__ qs,
+                                                           const uint8_t* __restrict__ kc,
+                                                           const uint8_t* __restrict__ ks,
+                                                           const uint8_t* __restrict__ vc,
+                                                           const uint8_t* __restrict__ vcs, int S, int Hq, int Hkv,
+                                                           float scale_log2, float* __restrict__ o_c,
+                                                           float* __restrict__ lse_c, int n_qtiles) {
+  __shared__ TileSmem sm[2];  // double buffer: tile it is read from sm[it & 1] while it+1 is loaded
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hf = lane >> 5;
   const int qtile = n_qtiles - 1 - (int)blockIdx.x;  // longest first
@@ -89,135 +239,39 @@ __global__ __launch_bounds__(256) void completed_kernel(const uint8_t* __restric
     }
   }
 
-  v16f oacc[4];
+  RowState st;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-  float T = -INFINITY;  // integer-valued running exponent
-  float lsum = 0.f;     // this lane's share of sum p
+    for (int i = 0; i < 16; ++i) st.o[dt][i] = 0.f;
+  st.T = -INFINITY;
+  st.lsum = 0.f;
 
+  uint4 pk0, pk1, pv0, pv1;
+  uint32_t psc;
+  if (ntiles > 0) {
+    TILE_LOAD(pk0, pk1, pv0, pv1, psc, 0);
+    store_tile(sm[0], pk0, pk1, pv0, pv1, psc, tid);
+  }
+  __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int kt0 = it * CB_BN;
-    __syncthreads();  // the previous tile has been consumed
-    {
-      const int r = tid >> 2, ch = (tid & 3) * 32;
-      const uint8_t* src = kc + (bhk * S + kt0 + r) * 128 + ch;
-      *reinterpret_cast<uint4*>(sm.k + r * CB_KROW + ch) = *reinterpret_cast<const uint4*>(src);
-      *reinterpret_cast<uint4*>(sm.k + r * CB_KROW + ch + 16) = *reinterpret_cast<const uint4*>(src + 16);
-      const int d = tid >> 1, hv = (tid & 1) * 32;
-      const uint8_t* vsrc = vc + (bhk * 128 + d) * S + kt0 + hv;
-      *reinterpret_cast<uint4*>(sm.v + d * CB_VROW + hv) = *reinterpret_cast<const uint4*>(vsrc);
-      *reinterpret_cast<uint4*>(sm.v + d * CB_VROW + hv + 16) = *reinterpret_cast<const uint4*>(vsrc + 16);
-      if (tid < 64) {
-        sm.ks[tid] = *reinterpret_cast<const uint32_t*>(ks + (bhk * S + kt0 + tid) * 4);
-      } else if (tid < 128) {
-        *reinterpret_cast<uint32_t*>(sm.vs + (tid - 64) * 4) =
-            *reinterpret_cast<const uint32_t*>(vcs + (bhk * (S / 32) + kt0 / 32) * 128 + (tid - 64) * 4);
-      }
-    }
+    // Prefetch the next tile (the last iteration fetches its own tile again; it is not stored).
+    const int kn = (it + 1 < ntiles) ? kt0 + CB_BN : kt0;
+    TILE_LOAD(pk0, pk1, pv0, pv1, psc, kn);
+    const TileSmem& cur = sm[it & 1];
+    if (kt0 + CB_BN <= e_w)
+      process_tile<true>(st, cur, qop, qsc, scale_log2, c, hf);
+    else if (kt0 < e_w)
+      process_tile<false>(st, cur, qop, qsc, scale_log2, c, hf);
+    if (it + 1 < ntiles) store_tile(sm[(it + 1) & 1], pk0, pk1, pv0, pv1, psc, tid);
     __syncthreads();
-    if (kt0 >= e_w) continue;  // wave-uniform: this wave's keys end before the tile
-    const bool second = kt0 + 32 < e_w;  // is the tile's second 32-key block completed for this wave?
-
-    // ---- S^T = K Q^T for the tile's two 32-key blocks --------------------------------------
-    v16f sacc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
-      if (kt == 1 && !second) continue;
-      const uint32_t ksw = sm.ks[32 * kt + c];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint8_t* kr = sm.k + (32 * kt + c) * CB_KROW + 64 * m + 16 * hf;
-        const v8i kop = make_v8i(*reinterpret_cast<const uint4*>(kr), *reinterpret_cast<const uint4*>(kr + 32));
-        const int ksc = (int)((ksw >> (8 * (2 * m + hf))) & 0xffu);
-        sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[m], sacc[kt], 0, 0, 0, ksc, 0, qsc[m]);
-      }
-    }
-    // Lane (c, hf), element i of block kt holds key kt0 + 32kt + 8(i/4) + 4hf + (i%4), query c.
-
-    // ---- p = 2^(t - T), block maxima, lazy rescale ------------------------------------------
-    float p[2][16];
-    float M0 = 0.f, M1 = 0.f;
-    for (int pass = 0; pass < 2; ++pass) {
-      const float negT = -T;
-      float pm0 = 0.f, pm1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[0][i] = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], scale_log2, negT));
-        pm0 = fmaxf(pm0, p[0][i]);
-        p[1][i] = second ? __builtin_amdgcn_exp2f(fmaf(sacc[1][i], scale_log2, negT)) : 0.f;
-        pm1 = fmaxf(pm1, p[1][i]);
-      }
-      uint32_t x = __builtin_bit_cast(uint32_t, pm0), y = __builtin_bit_cast(uint32_t, pm1);
-      swap32(x, y);  // lanes 0..31 now hold both halves of block 0, lanes 32..63 of block 1
-      uint32_t mo = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y)));
-      uint32_t mo2 = mo;
-      swap32(mo, mo2);  // every lane: mo = block-0 maximum, mo2 = block-1 maximum
-      M0 = __builtin_bit_cast(float, mo);
-      M1 = __builtin_bit_cast(float, mo2);
-      if (!__any(fmaxf(M0, M1) > CB_PMAX_LAZY)) break;
-      // Rare path: raise T to ceil(row max of t); rescale by the exact power of two 2^(T - Tn).
-      float mt = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        mt = fmaxf(mt, sacc[0][i] * scale_log2);
-        if (second) mt = fmaxf(mt, sacc[1][i] * scale_log2);
-      }
-      uint32_t a = __builtin_bit_cast(uint32_t, mt), a2 = a;
-      swap32(a, a2);
-      mt = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, a2));
-      const float Tn = fmaxf(T, ceilf(mt));
-      const float f = __builtin_amdgcn_exp2f(T - Tn);  // 0 on the first tile, else 2^-(integer)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= f;
-      lsum *= f;
-      T = Tn;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lsum += p[0][i] + p[1][i];
-
-    // ---- quantise P: one E8M0 per (query, 32-key block) --------------------------------------
-    // Exponent -127 is only reached by blocks whose largest p is below 2^-118; they use -126 so the
-    // conversion's power-of-two divisor stays a normal fp32 value.
-    const int k0 = max(e8m0_exponent(M0), -126), k1 = max(e8m0_exponent(M1), -126);
-    const float sc0 = u2f((uint32_t)(127 + k0) << 23), sc1 = u2f((uint32_t)(127 + k1) << 23);
-    uint32_t sl[8];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      sl[g] = pack4_e4m3_scaled(p[0][4 * g], p[0][4 * g + 1], p[0][4 * g + 2], p[0][4 * g + 3], sc0);
-      sl[4 + g] = pack4_e4m3_scaled(p[1][4 * g], p[1][4 * g + 1], p[1][4 * g + 2], p[1][4 * g + 3], sc1);
-    }
-    // Slot g holds keys 8g + 4hf + [0,4) of its block. The B operand of O^T wants, in lane hf,
-    // keys 16hf + [0,16) of block 0 then of block 1: trade slots 2,3 (6,7) of the lower half for
-    // slots 0,1 (4,5) of the upper half.
-    swap32(sl[0], sl[2]);
-    swap32(sl[1], sl[3]);
-    swap32(sl[4], sl[6]);
-    swap32(sl[5], sl[7]);
-    v8i pop;
-    pop[0] = (int)sl[0]; pop[1] = (int)sl[2]; pop[2] = (int)sl[1]; pop[3] = (int)sl[3];
-    pop[4] = (int)sl[4]; pop[5] = (int)sl[6]; pop[6] = (int)sl[5]; pop[7] = (int)sl[7];
-    const int psc = (hf ? k1 : k0) + 127;
-
-    // ---- O^T += V^T P^T over the four 32-column tiles of D -----------------------------------
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint8_t* vr = sm.v + (32 * dt + c) * CB_VROW + 16 * hf;
-      const v8i vop = make_v8i(*reinterpret_cast<const uint4*>(vr), *reinterpret_cast<const uint4*>(vr + 32));
-      const int vsc = sm.vs[hf * 128 + 32 * dt + c];
-      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, oacc[dt], 0, 0, 0, vsc, 0, psc);
-    }
   }
 
   // ---- epilogue: O_c = acc / l, lse_c = ln2 (T + log2 l) ---------------------------------------
-  uint32_t la = __builtin_bit_cast(uint32_t, lsum), lb = la;
-  swap32(la, lb);
-  const float ltot = __builtin_bit_cast(float, la) + __builtin_bit_cast(float, lb);
+  float la = st.lsum, lb = st.lsum;
+  swap32f(la, lb);
+  const float ltot = la + lb;
   if (!wave_valid) return;
   float* orow = o_c + (bhq * S + qw + c) * 128;
   const bool empty = (e_w == 0);
@@ -226,12 +280,11 @@ __global__ __launch_bounds__(256) void completed_kernel(const uint8_t* __restric
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // Lane (c, hf), element i of tile dt: column d = 32dt + 8(i/4) + 4hf + (i%4).
-      const float4 val = make_float4(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
-                                     oacc[dt][4 * g + 3] * inv);
+      const float4 val = make_float4(st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv, st.o[dt][4 * g + 2] * inv,
+                                     st.o[dt][4 * g + 3] * inv);
       *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * hf) = val;
     }
-  if (hf == 0) lse_c[bhq * S + qw + c] = empty ? -INFINITY : (T + log2f(ltot)) * 0.69314718055994530942f;
+  if (hf == 0) lse_c[bhq * S + qw + c] = empty ? -INFINITY : (st.T + log2f(ltot)) * 0.69314718055994530942f;
 }
 
 hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,

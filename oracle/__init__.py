@@ -52,8 +52,8 @@ def _load():
         lib.orc_quantize_rowwise.argtypes = [P, I, I, I, I, I64, I64, I64, P, P]
         lib.orc_quantize_v.argtypes = [P, I, I, I, I, I64, I64, I64, P, P, P, P]
         six = [P] * 6
-        lib.orc_attn_completed.argtypes = six + [I, I, I, I, I, F, P, I, I, P, P, D, P, D, ctypes.c_uint64]
-        lib.orc_attn_own.argtypes = six + [I, I, I, I, I, F, P, I, P, P]
+        lib.orc_attn_completed.argtypes = six + [I, I, I, I, I, F, P, I, I, P, P, D, P, P, D, ctypes.c_uint64]
+        lib.orc_attn_own.argtypes = six + [I, I, I, I, I, F, P, I, P, P, D, P, P, D, ctypes.c_uint64]
         lib.orc_attn_leaky.argtypes = six + [I, I, I, I, I, F, P, I, P, P]
         lib.orc_lse_merge.argtypes = [P, P, P, P, I64, I, P, P]
         raw = [P, I64, I64, I64] * 3
@@ -175,27 +175,37 @@ def attn_completed(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None, t_shift=0
                    score_err=SCORE_ERR, jitter=0.0, jitter_seed=0):
     """O7: completed-block partial (O_c [B,Hq,n,D], lse_c [B,Hq,n]) from codes in the ABI layouts.
 
-    With ``allowance`` also returns the R15 allowance [B,Hq,n,D]: the largest change of O_c that the
-    alternative valid P codes can make under a score error bound of ``score_err`` per product step.
-    ``jitter`` (test model of a kernel) moves each score by up to ``jitter`` times its bound."""
+    With ``allowance`` also returns the R15 allowance [B,Hq,n,D] (the largest change of O_c that the
+    hardware's dot-product error can make: alternative valid P codes, the normaliser, P.V
+    accumulation) and the bound of the lse error [B,Hq,n], for a score error of ``score_err`` per
+    product step. ``jitter`` (test model of a kernel) moves each score by up to ``jitter`` times its
+    bound."""
     B, _, S, D = qc.shape
     r, n = _rows_arg(rows, S)
     o, lse = _out(B, Hq, n, D)
     al = np.empty_like(o) if allowance else None
+    le = np.empty_like(lse) if allowance else None
     args = [np.ascontiguousarray(a) for a in (qc, qs, kc, ks, vc, vcs)]
     _load().orc_attn_completed(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, int(t_shift),
-                               _ptr(o), _ptr(lse), float(score_err), _ptr(al), float(jitter), int(jitter_seed))
-    return (o, lse, al) if allowance else (o, lse)
+                               _ptr(o), _ptr(lse), float(score_err), _ptr(al), _ptr(le), float(jitter),
+                               int(jitter_seed))
+    return (o, lse, al, le) if allowance else (o, lse)
 
 
-def attn_own(qc, qs, kc, ks, vt, vta, Hq, Hkv, scale, rows=None):
-    """O8: own-block partial (O_o, lse_o) on the token-normalised V."""
+def attn_own(qc, qs, kc, ks, vt, vta, Hq, Hkv, scale, rows=None, allowance=False, score_err=SCORE_ERR, jitter=0.0,
+             jitter_seed=0):
+    """O8: own-block partial (O_o, lse_o) on the token-normalised V. With ``allowance`` also the R15
+    allowance and lse error bound for a kernel whose own-block scores carry the hardware
+    dot-product error."""
     B, _, S, D = qc.shape
     r, n = _rows_arg(rows, S)
     o, lse = _out(B, Hq, n, D)
+    al = np.empty_like(o) if allowance else None
+    le = np.empty_like(lse) if allowance else None
     args = [np.ascontiguousarray(a) for a in (qc, qs, kc, ks, vt, vta)]
-    _load().orc_attn_own(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, _ptr(o), _ptr(lse))
-    return o, lse
+    _load().orc_attn_own(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, _ptr(o), _ptr(lse),
+                         float(score_err), _ptr(al), _ptr(le), float(jitter), int(jitter_seed))
+    return (o, lse, al, le) if allowance else (o, lse)
 
 
 def attn_leaky(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None):
@@ -260,19 +270,23 @@ def quantize_all(q, k, v) -> Quantized:
 def forward(q, k, v, scale, rows=None, quant: Quantized | None = None, score_err=SCORE_ERR):
     """The leak-free forward: quantise, completed partial, own partial, merge. Returns
     (O [B,Hq,n,D], lse [B,Hq,n], parts) where parts holds the partials, the quantised operands and
-    "allowance": the R15 allowance of the completed partial carried through the merge (its weight
-    w_c / (w_c + w_o) = e^(lse_c - lse))."""
+    "allowance": the R15 allowance of the merged output, i.e. each partial's allowance times its
+    merge weight w = e^(lse_part - lse), plus the first-order effect of the partials' lse errors on
+    the weights, w_c w_o |O_c - O_o| (err_c + err_o)."""
     qv, kv = _as_view(q), _as_view(k)
     Hq, Hkv = qv.H, kv.H
     z = quant if quant is not None else quantize_all(q, k, v)
-    oc, lc, al = attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, Hq, Hkv, scale, rows, allowance=True,
-                                score_err=score_err)
-    oo, lo = attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, Hq, Hkv, scale, rows)
+    oc, lc, alc, ec = attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, Hq, Hkv, scale, rows, allowance=True,
+                                     score_err=score_err)
+    oo, lo, alo, eo = attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, Hq, Hkv, scale, rows, allowance=True,
+                               score_err=score_err)
     o, lse = lse_merge(oc, lc, oo, lo)
     with np.errstate(invalid="ignore"):
         wc = np.where(np.isneginf(lc), 0.0, np.exp(lc - lse))
-    return o, lse, {"o_c": oc, "lse_c": lc, "o_o": oo, "lse_o": lo, "quant": z, "allowance_c": al,
-                    "allowance": al * wc[..., None]}
+    wo = np.exp(lo - lse)
+    al = wc[..., None] * alc + wo[..., None] * alo + (wc * wo * (ec + eo))[..., None] * np.abs(oc - oo)
+    return o, lse, {"o_c": oc, "lse_c": lc, "o_o": oo, "lse_o": lo, "quant": z, "allowance_c": alc,
+                    "allowance_o": alo, "allowance": al, "lse_err": wc * ec + wo * eo}
 
 
 def forward_leaky(q, k, v, scale, rows=None, quant: Quantized | None = None):

@@ -27,14 +27,16 @@
  *       full precision (not quantised), V from the token-normalised copy.
  *   R8  A row with no completed key (i < 32) has O_c = 0, lse_c = -inf.
  *   R9  GQA: q-head hq reads kv-head floor(hq / (Hq / Hkv)).
- *   R15 Several valid results: a kernel forms the scores t in fp32 from a
- *       hardware block-scaled FP8 dot product whose accumulation is not
- *       correctly rounded, so a P value lying within that error of an E4M3
- *       rounding midpoint (or a block maximum within it of an E8M0 step) has
- *       two valid codes. With `allowance` the completed partial also returns,
- *       per output element, the largest change any such alternative code can
- *       make; a score-error bound `score_err` per 64-wide product step (times
- *       the largest |q.k| product of the step) defines "within".
+ *   R15 Several valid results: a kernel forms the scores t from a hardware
+ *       block-scaled FP8 dot product whose accumulation is not correctly
+ *       rounded (error up to `score_err` times the largest product of each
+ *       64-wide step), and P.V with the same instruction. With `allowance` the
+ *       completed partial also returns, per output element, the largest change
+ *       those errors can make: (i) a P value within its score error of an E4M3
+ *       rounding midpoint, or a block maximum within it of an E8M0 step, has
+ *       two valid codes; (ii) the unquantised p in the normaliser l moves by
+ *       its score error; (iii) each 64-key step of P.V may be off by
+ *       score_err times its largest |p^ v| product.
  */
 #include "oracle.h"
 
@@ -273,11 +275,13 @@ static double jitter_unit(uint64_t seed, int64_t row, int64_t j) {
    used only to pin the allowance. */
 static void completed_row(const double* q, const double* K, const double* V, int i, int D, double sigma,
                           int quantize_p, int t_shift, int leaky, double score_err, double jitter,
-                          uint64_t jitter_seed, int64_t row_id, double* o, double* lse, double* allow) {
+                          uint64_t jitter_seed, int64_t row_id, double* o, double* lse, double* allow,
+                          double* lse_err) {
   int n = leaky ? i + 1 : 32 * (i / 32);
   for (int d = 0; d < D; ++d) o[d] = 0.0;
   if (allow)
     for (int d = 0; d < D; ++d) allow[d] = 0.0;
+  if (lse_err) *lse_err = 0.0;
   if (n == 0) { /* R8 */
     *lse = -INFINITY;
     return;
@@ -331,10 +335,25 @@ static void completed_row(const double* q, const double* K, const double* V, int
     for (int d = 0; d < D; ++d) o[d] += phat[j] * V[(int64_t)j * D + d];
   for (int d = 0; d < D; ++d) o[d] /= l;
   if (allow) {
+    /* (i) alternative codes */
     for (int j = 0; j < n; ++j)
       if (alt[j] > 0.0)
         for (int d = 0; d < D; ++d) allow[d] += alt[j] * fabs(V[(int64_t)j * D + d]);
+    /* (iii) P.V accumulation: per 64-key step, score_err times its largest |p^ v| product */
+    for (int g0 = 0; g0 < n; g0 += 64) {
+      int g1 = (g0 + 64 < n) ? g0 + 64 : n;
+      for (int d = 0; d < D; ++d) {
+        double mx = 0.0;
+        for (int j = g0; j < g1; ++j) mx = fmax(mx, fabs(phat[j] * V[(int64_t)j * D + d]));
+        allow[d] += score_err * mx;
+      }
+    }
     for (int d = 0; d < D; ++d) allow[d] /= l;
+    /* (ii) the normaliser: l = sum p moves by at most sum rel_j p_j */
+    double dl = 0.0;
+    for (int j = 0; j < n; ++j) dl += rel[j] * p[j];
+    for (int d = 0; d < D; ++d) allow[d] += fabs(o[d]) * dl / l;
+    if (lse_err) *lse_err = dl / l; /* |d lse| <= |dl| / l */
   }
   *lse = LN2 * (T + log2(l));
   free(t);
@@ -345,14 +364,22 @@ static void completed_row(const double* q, const double* K, const double* V, int
 }
 
 /* O8 -- own-block partial of one query row [TE#3865 Description, second
-   bullet], reading R7: keys 32*floor(i/32) .. i, full-precision softmax. */
-static void own_row(const double* q, const double* K, const double* Vt, int i, int D, double sigma, double* o,
-                    double* lse) {
+   bullet], reading R7: keys 32*floor(i/32) .. i, full-precision softmax.
+   With `allow`, also the R15 allowance for a kernel whose scores carry the
+   hardware dot-product error (each p_j moves by at most its relative bound
+   rel_j, so O_o moves by at most sum_j rel_j p_j |V_j - O_o| / l) and the
+   bound of its lse error (sum_j rel_j p_j / l). jitter: as for O7. */
+static void own_row(const double* q, const double* K, const double* Vt, int i, int D, double sigma, double score_err,
+                    double jitter, uint64_t jitter_seed, int64_t row_id, double* o, double* lse, double* allow,
+                    double* lse_err) {
   int j0 = 32 * (i / 32);
-  double s[32], p[32];
+  double s[32], p[32], rel[32];
   double m = -INFINITY;
   for (int j = j0; j <= i; ++j) {
     s[j - j0] = sigma * dot(q, K + (int64_t)j * D, D);
+    if (allow || jitter != 0.0)
+      rel[j - j0] = p_rel_bound(q, K + (int64_t)j * D, D, sigma, s[j - j0] * LOG2E, score_err);
+    if (jitter != 0.0) s[j - j0] += jitter * (rel[j - j0] / LN2) / LOG2E * jitter_unit(jitter_seed, row_id, j);
     m = fmax(m, s[j - j0]);
   }
   double l = 0.0;
@@ -366,6 +393,16 @@ static void own_row(const double* q, const double* K, const double* Vt, int i, i
     o[d] = acc / l;
   }
   *lse = m + log(l);
+  if (allow) {
+    double dl = 0.0;
+    for (int j = j0; j <= i; ++j) dl += rel[j - j0] * p[j - j0];
+    for (int d = 0; d < D; ++d) {
+      double a = 0.0;
+      for (int j = j0; j <= i; ++j) a += rel[j - j0] * p[j - j0] * fabs(Vt[(int64_t)j * D + d] - o[d]);
+      allow[d] = a / l;
+    }
+    if (lse_err) *lse_err = dl / l;
+  }
 }
 
 /* O9 -- merge through the log-sum-exps [TE#3865 Description, second bullet:
@@ -394,7 +431,8 @@ static int row_index(const int32_t* rows, int r) { return rows ? rows[r] : r; }
    token-major [B,H,S,D] tensors. */
 static void run_rows(int part, const double* Q, const double* K, const double* V, int B, int S, int Hq, int Hkv,
                      int D, float scale, const int32_t* rows, int nrows, int quantize_p, int t_shift,
-                     double score_err, double jitter, uint64_t jitter_seed, double* o, double* lse, double* allow) {
+                     double score_err, double jitter, uint64_t jitter_seed, double* o, double* lse, double* allow,
+                     double* lse_err) {
   assert(Hq % Hkv == 0);
   const int G = Hq / Hkv;
   const double sigma = (double)scale;
@@ -411,7 +449,8 @@ static void run_rows(int part, const double* Q, const double* K, const double* V
         const double* Vh = V + ((int64_t)b * Hkv + hk) * S * D;
         int64_t orow = ((int64_t)b * Hq + hq) * nrows + r;
         if (part == PART_OWN) {
-          own_row(q, Kh, Vh, i, D, sigma, o + orow * D, lse + orow);
+          own_row(q, Kh, Vh, i, D, sigma, score_err, jitter, jitter_seed, ((int64_t)b * Hq + hq) * S + i,
+                  o + orow * D, lse + orow, allow ? allow + orow * D : NULL, lse_err ? lse_err + orow : NULL);
         } else if (part == PART_TEXTBOOK) {
           double* s = (double*)malloc(sizeof(double) * (i + 1));
           double m = -INFINITY, l = 0.0;
@@ -431,7 +470,7 @@ static void run_rows(int part, const double* Q, const double* K, const double* V
         } else {
           completed_row(q, Kh, Vh, i, D, sigma, quantize_p, t_shift, part == PART_LEAKY, score_err, jitter,
                         jitter_seed, ((int64_t)b * Hq + hq) * S + i, o + orow * D, lse + orow,
-                        allow ? allow + orow * D : NULL);
+                        allow ? allow + orow * D : NULL, lse_err ? lse_err + orow : NULL);
         }
       }
 }
@@ -439,12 +478,12 @@ static void run_rows(int part, const double* Q, const double* K, const double* V
 void orc_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                         const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale,
                         const int32_t* rows, int nrows, int t_shift, double* o, double* lse, double score_err,
-                        double* allowance, double jitter, uint64_t jitter_seed) {
+                        double* allowance, double* lse_err, double jitter, uint64_t jitter_seed) {
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vcol(vc, vcs, B, Hkv, S, D);
   run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, t_shift, score_err, jitter,
-           jitter_seed, o, lse, allowance);
+           jitter_seed, o, lse, allowance, lse_err);
   free(Q);
   free(K);
   free(V);
@@ -456,7 +495,7 @@ void orc_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vcol(vc, vcs, B, Hkv, S, D);
-  run_rows(PART_LEAKY, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, 0, 0.0, 0.0, 0, o, lse, NULL);
+  run_rows(PART_LEAKY, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, 0, 0.0, 0.0, 0, o, lse, NULL, NULL);
   free(Q);
   free(K);
   free(V);
@@ -464,11 +503,13 @@ void orc_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, con
 
 void orc_attn_own(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
                   const uint8_t* vta, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
-                  int nrows, double* o, double* lse) {
+                  int nrows, double* o, double* lse, double score_err, double* allowance, double* lse_err,
+                  double jitter, uint64_t jitter_seed) {
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vtn(vt, vta, B, Hkv, S, D);
-  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, o, lse, NULL);
+  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, score_err, jitter, jitter_seed, o, lse,
+           allowance, lse_err);
   free(Q);
   free(K);
   free(V);
@@ -481,7 +522,7 @@ void orc_attn_reference(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh
   double* Q = bf16_tensor(q, qsb, qss, qsh, B, S, Hq, D);
   double* K = bf16_tensor(k, ksb, kss, ksh, B, S, Hkv, D);
   double* V = bf16_tensor(v, vsb, vss, vsh, B, S, Hkv, D);
-  run_rows(PART_TEXTBOOK, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, o, lse, NULL);
+  run_rows(PART_TEXTBOOK, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, o, lse, NULL, NULL);
   free(Q);
   free(K);
   free(V);
@@ -499,8 +540,8 @@ void orc_attn_identity(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh,
   double* oo = (double*)malloc(sizeof(double) * n * D);
   double* lc = (double*)malloc(sizeof(double) * n);
   double* lo = (double*)malloc(sizeof(double) * n);
-  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, oc, lc, NULL);
-  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, oo, lo, NULL);
+  run_rows(PART_COMPLETED, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, oc, lc, NULL, NULL);
+  run_rows(PART_OWN, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 0, 0, 0.0, 0.0, 0, oo, lo, NULL, NULL);
   orc_lse_merge(oc, lc, oo, lo, n, D, o, lse);
   free(oc);
   free(oo);

@@ -55,16 +55,20 @@ void orc_quantize_v(const uint16_t* v, int B, int S, int H, int D, int64_t sb, i
    allowance (may be NULL, else [B,Hq,nrows,D]): per element, the largest
    change of O_c that alternative valid P codes can make when a kernel's score
    error is bounded by score_err * (largest |q.k| product of each 64-wide step)
-   in log2 units (reading R15). jitter/jitter_seed: if jitter != 0, every score
-   is moved by jitter * its bound * u, u in [-1, 1] (test model of a kernel). */
+   in log2 units (reading R15); lse_err (may be NULL, else [B,Hq,nrows]) the
+   bound of the resulting lse error. jitter/jitter_seed: if jitter != 0, every
+   score is moved by jitter * its bound * u, u in [-1, 1] (test model of a kernel). */
 void orc_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                         const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale,
                         const int32_t* rows, int nrows, int t_shift, double* o, double* lse, double score_err,
-                        double* allowance, double jitter, uint64_t jitter_seed);
-/* O8: own-block partial on the token-normalised V. */
+                        double* allowance, double* lse_err, double jitter, uint64_t jitter_seed);
+/* O8: own-block partial on the token-normalised V. allowance/lse_err (may be
+   NULL): the R15 bounds for a kernel whose own-block scores carry the same
+   hardware dot-product error; jitter as for O7. */
 void orc_attn_own(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
                   const uint8_t* vta, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
-                  int nrows, double* o, double* lse);
+                  int nrows, double* o, double* lse, double score_err, double* allowance, double* lse_err,
+                  double jitter, uint64_t jitter_seed);
 /* O9: merge two partials through their log-sum-exps; n rows of D. */
 void orc_lse_merge(const double* oc, const double* lsec, const double* oo, const double* lseo, int64_t n, int D,
                    double* o, double* lse);

@@ -35,8 +35,8 @@ def _partials_case(inp, rows=None):
     oc, lc = mx.attn_fwd_completed_blocks(g["qc"], g["qs"], g["kc"], g["ks"], g["vc"], g["vcs"], w.scale)
     oo, lo = mx.attn_fwd_own_block(g["qc"], g["qs"], g["kc"], g["ks"], g["vt"], g["vta"], w.scale)
     torch.cuda.synchronize()
-    roc, rlc, ral = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale, rows,
-                                          allowance=True)
+    roc, rlc, ral, _ = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale, rows,
+                                             allowance=True)
     roo, rlo = oracle.attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, w.Hq, w.Hkv, w.scale, rows)
     sel = slice(None) if rows is None else rows
     goc = oc.double().cpu().numpy()[:, :, sel]
