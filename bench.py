@@ -1,16 +1,17 @@
 """Benchmark: leak-free causal MXFP8 attention forward on one MI355X.
 
 One step is one pass of the whole forward path over one batch: MXFP8 quantisation of Q, K (rowwise)
-and V (columnwise + token-normalised), the completed-block partial, the own-block partial and the
-LSE merge (bf16 output), each through the C ABI of libmxfa.so on torch's current stream. Inputs are
-seeded synthetic bf16 tensors already resident in HBM when the timed region starts.
+and V (columnwise + token-normalised), then the completed-block partial, the own-block partial and
+the LSE merge (bf16 output) -- by default in one fused kernel (`--path fused`), or as three separate
+kernels (`--path stepwise`) -- each call through the C ABI of libmxfa.so on torch's current stream.
+Inputs are seeded synthetic bf16 tensors already resident in HBM when the timed region starts.
 
 Workload (the configuration the published forward timings are quoted on): B=1, 16 query heads,
 4 KV heads, S=32768, D=128, BSHD, causal, V rows scaled by 2^e, e ~ U{-4..4} per (token, kv-head).
 
 Prints one JSON line. `value` is TFLOP/s of the whole forward with the FlashAttention causal count
-2*B*Hq*S^2*D; `roofline` is the completed-block kernel (the dominant one) against the MXFP8 MFMA
-peak, from HIP events around its launches in the timed steps; `cpu_baseline` times the fp64 CPU
+2*B*Hq*S^2*D; `roofline` is the attention kernel (the dominant one: fused, or completed-block when
+stepwise) against the MXFP8 MFMA peak, from HIP events around its launches in the timed steps; `cpu_baseline` times the fp64 CPU
 oracle on a bounded row sample of the same workload.
 """
 from __future__ import annotations
@@ -44,11 +45,11 @@ def own_pairs(B, Hq, S):
     return B * Hq * (S // 32) * (32 * 33 // 2)
 
 
-def read_traffic(kernel_source: str):
-    """HBM traffic of the completed-block kernel per launch from the committed PMC summary, or None
-    when the summary is missing or was taken on a different kernel source."""
+def read_traffic(kernel_source: str, kernel: str):
+    """HBM traffic of the attention kernel per launch from the committed PMC summary, or None when
+    the summary is missing or was taken on a different kernel source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "completed_kernel_gqa16x4_s32k_pmc.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_kernel_gqa16x4_s32k_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -90,6 +91,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa16x4_s32k_amplitudes")
+    ap.add_argument("--path", choices=["fused", "stepwise"], default="fused")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle CPU-baseline sample (0 skips)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -113,14 +115,16 @@ def main():
     kc, ks = torch.empty((B, Hkv, S, D), **u8), torch.empty((B, Hkv, S, D // 32), **u8)
     vc, vcs = torch.empty((B, Hkv, D, S), **u8), torch.empty((B, Hkv, S // 32, D), **u8)
     vt, vta = torch.empty((B, Hkv, S, D), **u8), torch.empty((B, Hkv, S), **u8)
-    oc, lc = torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)
-    oo, lo = torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)
+    stepwise_buffers = args.path == "stepwise"
+    oc, lc = (torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)) if stepwise_buffers else (None, None)
+    oo, lo = (torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)) if stepwise_buffers else (None, None)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, S), **f32)
     L = mx.lib()
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    names = ["quantize_q", "quantize_k", "quantize_v", "completed", "own_block", "merge"]
+    fused = args.path == "fused"
+    names = ["quantize_q", "quantize_k", "quantize_v"] + (["fused"] if fused else ["completed", "own_block", "merge"])
 
     def view(t):
         return mx.view_of(t, lay)
@@ -135,15 +139,23 @@ def main():
                                           ks.data_ptr(), None, None, sh),
             lambda: L.mxfa_mxfp8_quantize(v.data_ptr(), B, S, Hkv, D, *vv[4:], mx.V, vc.data_ptr(), vcs.data_ptr(),
                                           vt.data_ptr(), vta.data_ptr(), sh),
-            lambda: L.mxfa_attn_fwd_completed_blocks(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
-                                                     vc.data_ptr(), vcs.data_ptr(), B, S, Hq, Hkv, D, w.scale,
-                                                     oc.data_ptr(), lc.data_ptr(), sh),
-            lambda: L.mxfa_attn_fwd_own_block(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
-                                              vt.data_ptr(), vta.data_ptr(), B, S, Hq, Hkv, D, w.scale,
-                                              oo.data_ptr(), lo.data_ptr(), sh),
-            lambda: L.mxfa_lse_merge(oc.data_ptr(), lc.data_ptr(), oo.data_ptr(), lo.data_ptr(), B, S, Hq, D,
-                                     out.data_ptr(), *ov[4:], mx.OUT_BF16, lse.data_ptr(), sh),
         ]
+        if fused:
+            calls.append(lambda: L.mxfa_attn_fwd_fused(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                                       vc.data_ptr(), vcs.data_ptr(), vt.data_ptr(), vta.data_ptr(),
+                                                       B, S, Hq, Hkv, D, w.scale, out.data_ptr(), *ov[4:],
+                                                       mx.OUT_BF16, lse.data_ptr(), sh))
+        else:
+            calls += [
+                lambda: L.mxfa_attn_fwd_completed_blocks(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                                         vc.data_ptr(), vcs.data_ptr(), B, S, Hq, Hkv, D, w.scale,
+                                                         oc.data_ptr(), lc.data_ptr(), sh),
+                lambda: L.mxfa_attn_fwd_own_block(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                                  vt.data_ptr(), vta.data_ptr(), B, S, Hq, Hkv, D, w.scale,
+                                                  oo.data_ptr(), lo.data_ptr(), sh),
+                lambda: L.mxfa_lse_merge(oc.data_ptr(), lc.data_ptr(), oo.data_ptr(), lo.data_ptr(), B, S, Hq, D,
+                                         out.data_ptr(), *ov[4:], mx.OUT_BF16, lse.data_ptr(), sh),
+            ]
         for i, c in enumerate(calls):
             if evs is not None:
                 evs[i][0].record(stream)
@@ -171,7 +183,9 @@ def main():
     flops = 2.0 * B * Hq * S * S * D
     comp_flops = 512.0 * completed_pairs(B, Hq, S)
     own_flops = 512.0 * own_pairs(B, Hq, S)
-    achieved = comp_flops / (per["completed"] * 1e-3) / 1e12
+    attn_name = "fused" if fused else "completed"
+    attn_flops = comp_flops + own_flops if fused else comp_flops
+    achieved = attn_flops / (per[attn_name] * 1e-3) / 1e12
     n_q, n_kv = B * Hq * S, B * Hkv * S
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
     kernels = {
@@ -179,13 +193,16 @@ def main():
         "quantize_k": {"ms": per["quantize_k"], "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32), per["quantize_k"])},
         "quantize_v": {"ms": per["quantize_v"],
                        "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32 + 1 + 1 / 128), per["quantize_v"])},
-        "completed": {"ms": per["completed"], "TFLOP/s": achieved, "algorithmic_flop": comp_flops},
-        "own_block": {"ms": per["own_block"], "TFLOP/s": own_flops / (per["own_block"] * 1e-3) / 1e12,
-                      "GB/s": gbs(n_q * (D + 4 + D * 4 + 4) + n_kv * 2 * (D + 4), per["own_block"])},
-        "merge": {"ms": per["merge"], "GB/s": gbs(n_q * (2 * D * 4 + 2 * 4 + D * 2 + 4), per["merge"])},
     }
+    if fused:
+        kernels["fused"] = {"ms": per["fused"], "TFLOP/s": achieved, "algorithmic_flop": attn_flops}
+    else:
+        kernels["completed"] = {"ms": per["completed"], "TFLOP/s": achieved, "algorithmic_flop": comp_flops}
+        kernels["own_block"] = {"ms": per["own_block"], "TFLOP/s": own_flops / (per["own_block"] * 1e-3) / 1e12,
+                                "GB/s": gbs(n_q * (D + 4 + D * 4 + 4) + n_kv * 2 * (D + 4), per["own_block"])}
+        kernels["merge"] = {"ms": per["merge"], "GB/s": gbs(n_q * (2 * D * 4 + 2 * 4 + D * 2 + 4), per["merge"])}
     src = os.path.join(ROOT, "causal_mxfp8_block_amd", "csrc", "attn_completed.hip")
-    traffic = read_traffic(src)
+    traffic = read_traffic(src, attn_name)
     value = flops / (ms_step * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -201,11 +218,11 @@ def main():
         "dtype": "mxfp8",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "layout": lay,
-                   "causal": True, "values": w.values, "output": "bf16"},
+                   "causal": True, "values": w.values, "output": "bf16", "path": args.path},
         "pct_mfma_peak": round(100.0 * value / MFMA_FP8_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "completed_kernel", "launch_ms": round(per["completed"], 4)},
+                     "kernel": f"attn_kernel ({attn_name})", "launch_ms": round(per[attn_name], 4)},
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for n, d in kernels.items()},
         "cpu_baseline": None,

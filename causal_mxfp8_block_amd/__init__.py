@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.mxfa_attn_fwd_own_block.restype = I
         L.mxfa_lse_merge.argtypes = [P, P, P, P, I, I, I, I, P, I64, I64, I64, I, P, P]
         L.mxfa_lse_merge.restype = I
+        L.mxfa_attn_fwd_fused.argtypes = [P] * 8 + [I, I, I, I, I, F, P, I64, I64, I64, I, P, P]
+        L.mxfa_attn_fwd_fused.restype = I
         L.mxfa_attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
         L.mxfa_attn_fwd_workspace_bytes.restype = SZ
         L.mxfa_attn_fwd.argtypes = [P, I64, I64, I64] * 3 + [I, I, I, I, I, F, P, SZ, P, I64, I64, I64, I, P, P]
@@ -168,13 +170,30 @@ def lse_merge(o_c, lse_c, o_o, lse_o, out_dtype=torch.bfloat16, layout: str = "b
     return out, lse
 
 
+def attn_fwd_fused(qc, qs, kc, ks, vc, vcs, vt, vta, softmax_scale: float | None = None, out_dtype=torch.bfloat16,
+                   layout: str = "bshd", out=None, lse=None):
+    """Both partials and the merge in one kernel, from the codes: (out in ``layout``, lse [B,Hq,S])."""
+    B, Hq, S, D = qc.shape
+    Hkv = kc.shape[1]
+    scale = default_scale(D) if softmax_scale is None else softmax_scale
+    if out is None:
+        shape = (B, S, Hq, D) if layout == "bshd" else (S, B, Hq, D)
+        out = torch.empty(shape, dtype=out_dtype, device=qc.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=qc.device)
+    _, _, _, _, osb, oss, osh = view_of(out, layout)
+    _check(lib().mxfa_attn_fwd_fused(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vcs), _p(vt), _p(vta), B, S, Hq, Hkv,
+                                     D, scale, _p(out), osb, oss, osh, _out_code(out.dtype), _p(lse), _stream(qc)))
+    return out, lse
+
+
 def attn_fwd_workspace_bytes(B: int, S: int, Hq: int, Hkv: int, D: int = 128) -> int:
     return int(lib().mxfa_attn_fwd_workspace_bytes(B, S, Hq, Hkv, D))
 
 
 def attn_fwd(q, k, v, softmax_scale: float | None = None, layout: str = "bshd", out_dtype=torch.bfloat16,
              workspace=None, out=None, lse=None):
-    """The whole leak-free forward in one call (quantise Q, K, V; both partials; merge).
+    """The whole leak-free forward in one call (quantise Q, K, V; then the fused attention).
 
     q [B,S,Hq,D], k and v [B,S,Hkv,D] bf16 in ``layout``; returns (out in q's layout, lse [B,Hq,S])."""
     B, S, Hq, D, qsb, qss, qsh = view_of(q, layout)

@@ -102,7 +102,6 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct Workspace {
   uint8_t *qc, *qs, *kc, *ks, *vc, *vcs, *vt, *vta;
-  float *oc, *lc, *oo, *lo;
   size_t bytes;
 };
 
@@ -123,10 +122,6 @@ Workspace carve(void* base, int B, int S, int Hq, int Hkv) {
   w.vcs = take(nk * 4);
   w.vt = take(nk * 128);
   w.vta = take(nk);
-  w.oc = reinterpret_cast<float*>(take(nq * 128 * 4));
-  w.lc = reinterpret_cast<float*>(take(nq * 4));
-  w.oo = reinterpret_cast<float*>(take(nq * 128 * 4));
-  w.lo = reinterpret_cast<float*>(take(nq * 4));
   w.bytes = off;
   return w;
 }
@@ -236,6 +231,27 @@ MXFA_EXPORT int mxfa_lse_merge(const float* o_c, const float* lse_c, const float
                     "lse_merge launch");
 }
 
+MXFA_EXPORT int mxfa_attn_fwd_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                    const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta,
+                                    int B, int S, int Hq, int Hkv, int D, float softmax_scale, void* out,
+                                    int64_t osb, int64_t oss, int64_t osh, int out_dtype, float* lse_out,
+                                    void* stream) {
+  g_last_error.clear();
+  TRY(check_attn_shape(B, S, Hq, Hkv, D));
+  const char* n[] = {"qc", "qs", "kc", "ks", "vc", "vcs", "vt", "vta"};
+  const void* p[] = {qc, qs, kc, ks, vc, vcs, vt, vta};
+  TRY(check_ptrs(n, p, 8));
+  if (out_dtype != MXFA_OUT_BF16 && out_dtype != MXFA_OUT_F32)
+    return fail(MXFA_ERR_UNSUPPORTED, "unknown output dtype %d", out_dtype);
+  TRY(check_view("out", out, B, S, Hq, osb, oss, osh, out_dtype == MXFA_OUT_BF16 ? 8 : 4));
+  if (lse_out && !aligned16(lse_out)) return fail(MXFA_ERR_ALIGN, "lse_out is not 16-byte aligned");
+  TRY(check_device());
+  return hip_status(mxfa::launch_attn_fused(qc, qs, kc, ks, vc, vcs, vt, vta, B, S, Hq, Hkv, softmax_scale, out, osb,
+                                            oss, osh, out_dtype == MXFA_OUT_BF16, lse_out,
+                                            static_cast<hipStream_t>(stream)),
+                    "attn_fwd_fused launch");
+}
+
 MXFA_EXPORT size_t mxfa_attn_fwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D) {
   if (D != 128 || B < 1 || S < 1 || Hq < 1 || Hkv < 1) return 0;
   return carve(nullptr, B, S, Hq, Hkv).bytes;
@@ -267,13 +283,8 @@ MXFA_EXPORT int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t q
   TRY(hip_status(mxfa::launch_quantize_rowwise(q16, B, S, Hq, qsb, qss, qsh, w.qc, w.qs, st), "quantize q"));
   TRY(hip_status(mxfa::launch_quantize_rowwise(k16, B, S, Hkv, ksb, kss, ksh, w.kc, w.ks, st), "quantize k"));
   TRY(hip_status(mxfa::launch_quantize_v(v16, B, S, Hkv, vsb, vss, vsh, w.vc, w.vcs, w.vt, w.vta, st), "quantize v"));
-  TRY(hip_status(mxfa::launch_attn_completed(w.qc, w.qs, w.kc, w.ks, w.vc, w.vcs, B, S, Hq, Hkv, softmax_scale, w.oc,
-                                             w.lc, st),
-                 "completed blocks"));
-  TRY(hip_status(mxfa::launch_attn_own_block(w.qc, w.qs, w.kc, w.ks, w.vt, w.vta, B, S, Hq, Hkv, softmax_scale, w.oo,
-                                             w.lo, st),
-                 "own block"));
-  return hip_status(mxfa::launch_lse_merge(w.oc, w.lc, w.oo, w.lo, B, S, Hq, out, osb, oss, osh,
-                                           out_dtype == MXFA_OUT_BF16, lse_out, st),
-                    "lse merge");
+  return hip_status(mxfa::launch_attn_fused(w.qc, w.qs, w.kc, w.ks, w.vc, w.vcs, w.vt, w.vta, B, S, Hq, Hkv,
+                                           softmax_scale, out, osb, oss, osh, out_dtype == MXFA_OUT_BF16, lse_out,
+                                           st),
+                    "fused attention");
 }

@@ -201,27 +201,46 @@ __device__ __forceinline__ void process_tile(RowState& st, const TileSmem& t, co
   }
 }
 
-__global__ __launch_bounds__(256, 2) void completed_kernel(const uint8_t* __restrict__ qc,
-                                                           const uint8_t* __restrict__ qs,
-                                                           const uint8_t* __restrict__ kc,
-                                                           const uint8_t* __restrict__ ks,
-                                                           const uint8_t* __restrict__ vc,
-                                                           const uint8_t* __restrict__ vcs, int S, int Hq, int Hkv,
-                                                           float scale_log2, float* __restrict__ o_c,
-                                                           float* __restrict__ lse_c, int n_qtiles) {
-  __shared__ TileSmem sm[2];  // double buffer: tile it is read from sm[it & 1] while it+1 is loaded
+struct AttnParams {
+  const uint8_t *qc, *qs, *kc, *ks, *vc, *vcs;  // rowwise Q/K and columnwise V codes/scales
+  const uint8_t *vt, *vta;                       // token-normalised V (fused epilogue only)
+  int S, Hq, Hkv, n_qtiles;
+  float scale_log2;                              // softmax_scale * log2(e)
+  float *o_c, *lse_c;                            // completed partial (unfused)
+  void* out;                                     // final output view (fused)
+  int64_t osb, oss, osh;
+  int out_bf16;
+  float* lse_out;                                // may be null (fused)
+};
+
+// LDS: the double-buffered K/V tiles of the main loop, reused afterwards (fused epilogue) for each
+// wave's decoded token-normalised own-block V, 32 keys x 128 columns of fp32.
+constexpr int CB_LDS_BYTES = 4 * 32 * 128 * 4;
+static_assert(2 * sizeof(TileSmem) <= CB_LDS_BYTES, "tile buffers must fit the LDS block");
+
+// kFused = false: the completed-block partial (O_c, lse_c). kFused = true: the whole attention of
+// the row: completed blocks, the own block on the token-normalised V (TE#3865 Description, second
+// bullet), and the merge through the log-sum-exps, written once in the output's layout.
+template <bool kFused>
+__global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
+  __shared__ __align__(16) uint8_t lds[kFused ? CB_LDS_BYTES : 2 * sizeof(TileSmem)];
+  TileSmem* sm = reinterpret_cast<TileSmem*>(lds);  // sm[0], sm[1]
+  const int S = P.S;
+  const uint8_t *__restrict__ kc = P.kc, *__restrict__ ks = P.ks, *__restrict__ vc = P.vc,
+                *__restrict__ vcs = P.vcs;
+  const float scale_log2 = P.scale_log2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hf = lane >> 5;
-  const int qtile = n_qtiles - 1 - (int)blockIdx.x;  // longest first
+  const int qtile = P.n_qtiles - 1 - (int)blockIdx.x;  // longest first
   const int hq = blockIdx.y, b = blockIdx.z;
-  const int hk = hq / (Hq / Hkv);
+  const int hk = hq / (P.Hq / P.Hkv);
   const int q0 = qtile * CB_BM;
-  const int qw = q0 + 32 * wave;          // first query of this wave; its keys are j < qw
+  const int qw = q0 + 32 * wave;          // first query of this wave; its completed keys are j < qw
   const bool wave_valid = qw < S;
   const int e_w = wave_valid ? qw : 0;
   const int e_wg = min(q0 + 96, S - 32);  // key range end of the last valid wave
   const int ntiles = (e_wg + CB_BN - 1) / CB_BN;
-  const int64_t bhq = (int64_t)b * Hq + hq, bhk = (int64_t)b * Hkv + hk;
+  const int64_t bhq = (int64_t)b * P.Hq + hq, bhk = (int64_t)b * P.Hkv + hk;
 
   // Q^T operand (B of S^T = K Q^T) for the two 64-wide K steps over D. Lane (c, hf) holds bytes
   // d = 64m + 16hf + [0,16) and 64m + 32 + 16hf + [0,16) of query qw + c; its scale is that of
@@ -229,8 +248,8 @@ __global__ __launch_bounds__(256, 2) void completed_kernel(const uint8_t* __rest
   v8i qop[2] = {};
   int qsc[2] = {127, 127};
   if (wave_valid) {
-    const uint8_t* qrow = qc + (bhq * S + qw + c) * 128;
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(qs + (bhq * S + qw + c) * 4);
+    const uint8_t* qrow = P.qc + (bhq * S + qw + c) * 128;
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(P.qs + (bhq * S + qw + c) * 4);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       qop[m] = make_v8i(*reinterpret_cast<const uint4*>(qrow + 64 * m + 16 * hf),
@@ -268,32 +287,162 @@ __global__ __launch_bounds__(256, 2) void completed_kernel(const uint8_t* __rest
     __syncthreads();
   }
 
-  // ---- epilogue: O_c = acc / l, lse_c = ln2 (T + log2 l) ---------------------------------------
   float la = st.lsum, lb = st.lsum;
   swap32f(la, lb);
-  const float ltot = la + lb;
-  if (!wave_valid) return;
-  float* orow = o_c + (bhq * S + qw + c) * 128;
-  const bool empty = (e_w == 0);
-  const float inv = empty ? 0.f : 1.0f / ltot;
+  const float lc_tot = la + lb;       // l of the completed partial (both lane halves)
+  const bool empty = (e_w == 0);      // rows 0..31 have no completed key
+
+  if (!kFused) {
+    if (!wave_valid) return;
+    float* orow = P.o_c + (bhq * S + qw + c) * 128;
+    const float inv = empty ? 0.f : 1.0f / lc_tot;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 val = make_float4(st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv, st.o[dt][4 * g + 2] * inv,
-                                     st.o[dt][4 * g + 3] * inv);
-      *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * hf) = val;
+      for (int g = 0; g < 4; ++g) {
+        // Lane (c, hf), element 4g + r of tile dt: column d = 32dt + 8g + 4hf + r.
+        const float4 val = make_float4(st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv,
+                                       st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv);
+        *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * hf) = val;
+      }
+    if (hf == 0) P.lse_c[bhq * S + qw + c] = empty ? -INFINITY : (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
+    return;
+  } else {
+    // ---- own block: keys qw .. qw+31, query qw + c sees keys up to itself ----------------------
+    float* vown = reinterpret_cast<float*>(lds) + wave * (32 * 128);  // this wave's 32 x 128 fp32
+    v16f so;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) so[i] = 0.f;
+    if (wave_valid) {
+      // scores S^T = K_own Q^T on the same block-scaled FP8 MFMA as the completed blocks
+      const uint8_t* krow = kc + (bhk * S + qw + c) * 128;
+      const uint32_t ksw = *reinterpret_cast<const uint32_t*>(ks + (bhk * S + qw + c) * 4);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const v8i kop = make_v8i(*reinterpret_cast<const uint4*>(krow + 64 * m + 16 * hf),
+                                 *reinterpret_cast<const uint4*>(krow + 64 * m + 32 + 16 * hf));
+        const int ksc = (int)((ksw >> (8 * (2 * m + hf))) & 0xffu);
+        so = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[m], so, 0, 0, 0, ksc, 0, qsc[m]);
+      }
+      // decode the token-normalised V rows of the block: lane -> key lane/2, 64 columns
+      const int j = lane >> 1, d0 = (lane & 1) * 64;
+      const uint8_t* vrow = P.vt + (bhk * S + qw + j) * 128 + d0;
+      const float amp = e8m0_to_f32(P.vta[bhk * S + qw + j]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(vrow + 16 * q);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float4 f = make_float4(e4m3_to_f32(ww[r] & 0xffu) * amp, e4m3_to_f32((ww[r] >> 8) & 0xffu) * amp,
+                                       e4m3_to_f32((ww[r] >> 16) & 0xffu) * amp, e4m3_to_f32(ww[r] >> 24) * amp);
+          *reinterpret_cast<float4*>(vown + j * 128 + d0 + 16 * q + 4 * r) = f;
+        }
+      }
     }
-  if (hf == 0) lse_c[bhq * S + qw + c] = empty ? -INFINITY : (st.T + log2f(ltot)) * 0.69314718055994530942f;
+    __syncthreads();  // decoded rows visible to the whole wave
+    if (!wave_valid) return;
+    // softmax over the own block in the log2 domain; element i holds key 8(i/4) + 4hf + (i%4)
+    float t[16];
+    float mo = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = 8 * (i >> 2) + 4 * hf + (i & 3);
+      t[i] = (j <= c) ? so[i] * scale_log2 : -INFINITY;
+      mo = fmaxf(mo, t[i]);
+    }
+    float mo2 = mo;
+    swap32f(mo, mo2);
+    mo = fmaxf(mo, mo2);  // row max (key c itself is always visible)
+    float pa[16];
+    float lo = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      pa[i] = __builtin_amdgcn_exp2f(t[i] - mo);  // masked keys: exp2(-inf) = 0
+      lo += pa[i];
+    }
+    float lo2 = lo;
+    swap32f(lo, lo2);
+    lo += lo2;
+    // ---- merge weights through the log-sum-exps (log2 units) ----------------------------------
+    const float l2c = empty ? -INFINITY : st.T + log2f(lc_tot);
+    const float l2o = mo + log2f(lo);
+    const float M = fmaxf(l2c, l2o);
+    const float wc = empty ? 0.f : __builtin_amdgcn_exp2f(l2c - M);
+    const float wo = __builtin_amdgcn_exp2f(l2o - M);
+    const float inv = 1.0f / (wc + wo);
+    const float fc = empty ? 0.f : wc * inv / lc_tot, fo = wo * inv / lo;
+    const int q = qw + c;
+    const int64_t off = b * P.osb + (int64_t)q * P.oss + hq * P.osh + 4 * hf;
+    // ---- own O^T = V^T P^T in fp32 with v_mfma_f32_32x32x2_f32 ---------------------------------
+    // Step u contracts the two keys 8(u/4) + (u%4) (k = 0) and 8(u/4) + 4 + (u%4) (k = 1): lane
+    // (c, hf) supplies p of its query c for key k = hf, exactly pa[u]; as the A operand the same
+    // lane supplies V^t[key k = hf][column 32dt + c]. The result has the layout of st.o[dt].
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      v16f oo;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oo[e] = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = 8 * (u >> 2) + 4 * hf + (u & 3);
+        const float a = vown[j * 128 + 32 * dt + c];
+        oo = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pa[u], oo, 0, 0, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = st.o[dt][4 * g + e] * fc + oo[4 * g + e] * fo;
+        const int64_t o = off + 32 * dt + 8 * g;
+        if (P.out_bf16) {
+          uint2 pk;
+          pk.x = f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16);
+          pk.y = f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + o) = pk;
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(P.out) + o) = make_float4(r[0], r[1], r[2], r[3]);
+        }
+      }
+    }
+    if (hf == 0 && P.lse_out) P.lse_out[bhq * S + q] = (M + log2f(wc + wo)) * 0.69314718055994530942f;
+  }
+}
+
+static AttnParams base_params(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                              const uint8_t* vc, const uint8_t* vcs, int S, int Hq, int Hkv, float softmax_scale) {
+  AttnParams p{};
+  p.qc = qc; p.qs = qs; p.kc = kc; p.ks = ks; p.vc = vc; p.vcs = vcs;
+  p.S = S; p.Hq = Hq; p.Hkv = Hkv;
+  p.n_qtiles = (S + CB_BM - 1) / CB_BM;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  return p;
 }
 
 hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                  const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv,
                                  float softmax_scale, float* o_c, float* lse_c, hipStream_t stream) {
-  const int n_qtiles = (S + CB_BM - 1) / CB_BM;
-  const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
-  completed_kernel<<<dim3((unsigned)n_qtiles, (unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(
-      qc, qs, kc, ks, vc, vcs, S, Hq, Hkv, scale_log2, o_c, lse_c, n_qtiles);
+  AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, S, Hq, Hkv, softmax_scale);
+  p.o_c = o_c;
+  p.lse_c = lse_c;
+  attn_kernel<false><<<dim3((unsigned)p.n_qtiles, (unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                             const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B,
+                             int S, int Hq, int Hkv, float softmax_scale, void* out, int64_t osb, int64_t oss,
+                             int64_t osh, int out_bf16, float* lse_out, hipStream_t stream) {
+  AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, S, Hq, Hkv, softmax_scale);
+  p.vt = vt;
+  p.vta = vta;
+  p.out = out;
+  p.osb = osb;
+  p.oss = oss;
+  p.osh = osh;
+  p.out_bf16 = out_bf16;
+  p.lse_out = lse_out;
+  attn_kernel<true><<<dim3((unsigned)p.n_qtiles, (unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 

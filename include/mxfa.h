@@ -99,12 +99,24 @@ int mxfa_lse_merge(const float* o_c, const float* lse_c, const float* o_o, const
                    int D, void* out, int64_t osb, int64_t oss, int64_t osh, int out_dtype, float* lse_out,
                    void* stream);
 
-/* Bytes of workspace mxfa_attn_fwd needs (codes, scales and fp32 partials, 256-byte aligned parts). */
+/* attn_fwd_fused -- both partials and their merge in one kernel (TE #3865 Description, both
+ * bullets): per row, the completed blocks as in attn_fwd_completed_blocks, then the row's own block
+ * on the token-normalised V (scores on the same block-scaled FP8 product, softmax and P.V in fp32,
+ * P not quantised), merged through the log-sum-exps in registers; nothing but the final output and
+ * LSE is written. Inputs: the rowwise Q/K codes, the columnwise V codes and the token-normalised V
+ * codes in the layouts above. out is a [B,S,Hq,D] view (strides osb, oss, osh) written as bf16
+ * (round to nearest even) or fp32 per out_dtype; lse_out fp32 [B,Hq,S] may be NULL. */
+int mxfa_attn_fwd_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                        const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B, int S,
+                        int Hq, int Hkv, int D, float softmax_scale, void* out, int64_t osb, int64_t oss,
+                        int64_t osh, int out_dtype, float* lse_out, void* stream);
+
+/* Bytes of workspace mxfa_attn_fwd needs (the MXFP8 codes and scales, 256-byte aligned parts). */
 size_t mxfa_attn_fwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D);
 
-/* attn_fwd -- the whole forward: the three quantisations, both partials and the merge, in that order
- * on `stream`, using `workspace` (at least mxfa_attn_fwd_workspace_bytes, 256-byte aligned) for the
- * intermediates. q [B,S,Hq,D], k and v [B,S,Hkv,D] bf16 views; out is a [B,S,Hq,D] view. */
+/* attn_fwd -- the whole forward: the three quantisations, then attn_fwd_fused, in that order on
+ * `stream`, using `workspace` (at least mxfa_attn_fwd_workspace_bytes, 256-byte aligned) for the
+ * codes. q [B,S,Hq,D], k and v [B,S,Hkv,D] bf16 views; out is a [B,S,Hq,D] view. */
 int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const void* k, int64_t ksb, int64_t kss,
                   int64_t ksh, const void* v, int64_t vsb, int64_t vss, int64_t vsh, int B, int S, int Hq, int Hkv,
                   int D, float softmax_scale, void* workspace, size_t workspace_bytes, void* out, int64_t osb,

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["mxfa_mxfp8_quantize", "mxfa_attn_fwd_completed_blocks", "mxfa_attn_fwd_own_block",
-              "mxfa_lse_merge", "mxfa_attn_fwd", "mxfa_attn_fwd_workspace_bytes", "mxfa_status_string",
+              "mxfa_lse_merge", "mxfa_attn_fwd", "mxfa_attn_fwd_fused", "mxfa_attn_fwd_workspace_bytes",
+              "mxfa_status_string",
               "mxfa_last_error"]:
         assert n in names
 

@@ -122,17 +122,27 @@ def test_bf16_output_is_rne_of_f32_output():
     assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(l16, l32)
 
 
-def test_stepwise_equals_fused_entry():
-    """attn_fwd equals the five calls made one by one, bit for bit."""
-    inp = make_inputs(custom(1, 4, 1, 192, seed=12))
+def test_fused_entry_equals_attn_fwd_and_stepwise_path_matches_oracle():
+    """attn_fwd = quantise + attn_fwd_fused, bit for bit; the stepwise path (two partials and the
+    merge as separate kernels) and the fused one both meet the oracle."""
+    inp = make_inputs(custom(2, 4, 1, 224, values="token_amplitudes", seed=12))
+    w = inp.workload
     q, k, v = (to_dev(getattr(inp, n)) for n in ("q", "k", "v"))
     out, lse = mx.attn_fwd(q, k, v, out_dtype=torch.float32)
     g = gpu_quantize(inp)
+    of, lf = mx.attn_fwd_fused(g["qc"], g["qs"], g["kc"], g["ks"], g["vc"], g["vcs"], g["vt"], g["vta"],
+                               out_dtype=torch.float32)
     oc, lc = mx.attn_fwd_completed_blocks(g["qc"], g["qs"], g["kc"], g["ks"], g["vc"], g["vcs"])
     oo, lo = mx.attn_fwd_own_block(g["qc"], g["qs"], g["kc"], g["ks"], g["vt"], g["vta"])
     o2, l2 = mx.lse_merge(oc, lc, oo, lo, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    assert torch.equal(out, of) and torch.equal(lse, lf)
+    ro, rl, parts = oracle.forward(inp.q, inp.k, inp.v, w.scale)
+    rms = np.sqrt(np.mean(ro ** 2))
+    for name, o_, l_ in (("fused", of, lf), ("stepwise", o2, l2)):
+        go = o_.double().cpu().numpy().transpose(0, 2, 1, 3)
+        assert report(name, go, ro, rms, allowance=parts["allowance"], tol=TOL) <= TOL
+        assert np.max(np.abs(l_.double().cpu().numpy() - rl)) < 1e-3
 
 
 def test_causality_every_t_tiny():
