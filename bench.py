@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--workload", default="gqa16x4_s32k_amplitudes")
     ap.add_argument("--path", choices=["fused", "stepwise"], default="fused")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle CPU-baseline sample (0 skips)")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times): the calibration for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -100,6 +102,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_only:
+        n = args.copy_only << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
+        return
     import causal_mxfp8_block_amd as mx
     from causal_mxfp8_block_amd.inputs import WORKLOADS, make_inputs
 

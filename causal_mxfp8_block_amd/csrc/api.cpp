@@ -59,8 +59,9 @@ int check_attn_shape(int B, int S, int Hq, int Hkv, int D) {
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return fail(MXFA_ERR_SHAPE, "B, S, Hq, Hkv must be >= 1");
   if (S % 32 != 0) return fail(MXFA_ERR_SHAPE, "S = %d is not a multiple of 32", S);
   if (Hq % Hkv != 0) return fail(MXFA_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
-  if ((int64_t)B * Hq > 65535 * 64 || Hq > 65535 || B > 65535)
-    return fail(MXFA_ERR_SHAPE, "B = %d, Hq = %d exceed the launch grid", B, Hq);
+  if ((int64_t)B * Hq > 65535 * 64 || Hq > 65535 || B > 65535 ||
+      (int64_t)B * Hq * ((S + 127) / 128) > 0x7fffffff)
+    return fail(MXFA_ERR_SHAPE, "B = %d, Hq = %d, S = %d exceed the launch grid", B, Hq, S);
   return MXFA_OK;
 }
 

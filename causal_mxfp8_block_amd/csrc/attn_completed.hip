@@ -9,22 +9,34 @@
 //    [0, 32*cb) with no per-element mask: the completed-block mask is block-granular.
 //  * Scores are computed transposed, S^T = K . Q^T, with the block-scaled FP8 MFMA
 //    v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, one E8M0 per 32 along D on both sides). The
-//    accumulator then holds one query per lane (lane & 31) and 16 keys per 32-key tile, so row
+//    accumulator then holds one query per lane (lane & 31) and 16 keys per 32-key block, so row
 //    statistics are lane-local up to one exchange with lane ^ 32 (v_permlane32_swap).
+//  * The K rows of each 32-key block sit in LDS in a permuted order chosen so that accumulator
+//    element i of lane (c, hf) is key 16hf + i: exactly the bytes lane (c, hf) must supply as the
+//    B operand of O^T = V^T . P^T. The E4M3 codes of P therefore go into that MFMA where they were
+//    computed, with no cross-lane traffic.
 //  * Online softmax in the log2 domain with an integer running exponent T: p = 2^(t - T). T is
-//    raised only when a block maximum would exceed 2^8 (lazy rescale); the E8M0 quantisation of P
+//    raised only when a block maximum of p would exceed 2^8 (lazy rescale); the E8M0 quantisation of P
 //    commutes with powers of two, so the P codes do not depend on T.
-//  * P is quantised to E4M3 with one E8M0 per (query, 32-key block) by the scaled conversion
-//    v_cvt_scalef32_pk_fp8_f32; four v_permlane32_swaps move the codes into the B-operand layout of
-//    O^T = V^T . P^T (block-scaled FP8 MFMA again, V columnwise codes keys-contiguous per column).
+//  * The E8M0 exponent of each (query, 32-key block) of P comes from the block maximum taken on the
+//    raw scores: fma and v_exp_f32 are both monotone (the latter checked exhaustively on [-160, 10]),
+//    so 2^(max t - T) is exactly the largest p of the block. The block's exponent k is then folded
+//    into the exponential, p / 2^k = 2^(t - T - k), so the plain v_cvt_pk_fp8_f32 gives the E4M3
+//    codes; the normaliser sums p / 2^k per block and rescales the two block sums by 2^k. P.V is
+//    the block-scaled FP8 MFMA again, on the columnwise V codes (keys contiguous per column).
 //  * O^T leaves one query per lane too, so the rescale and the final 1/l are per-lane scalars.
 //  * K and V tiles of 64 keys are staged in LDS once per workgroup and shared by the 4 waves; the
 //    LDS is double-buffered and the next tile's global loads are in flight while the current tile
-//    computes, so one barrier per tile remains.
-//  * Two workgroups per CU (two waves per SIMD) so one wave's softmax overlaps another's MFMAs.
+//    computes, one barrier per tile.
+//  * Two workgroups per CU (two waves per SIMD, 212 VGPRs each): the softmax VALU work of one wave
+//    overlaps the MFMAs and memory waits of the other.
 //  * Full tiles and the half tile at the end of a wave's range are separate code paths, so the
 //    common path has no per-element select.
-//  * Workgroups are launched longest-first (the causal work of a query tile grows with its index).
+//  * One-dimensional grid in global longest-first order: all (batch, head) pairs of the last query
+//    tile, then of the one before, and so on (the causal work of a query tile grows with its
+//    index), so the machine drains evenly. Consecutive workgroup ids go to different XCDs in turn;
+//    the pair index is permuted so that the workgroups one XCD receives are adjacent (batch, head)
+//    pairs, i.e. query heads that share a KV head under GQA, which share K/V in that XCD's L2.
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,7 +52,7 @@ struct __align__(16) TileSmem {
   uint8_t k[CB_BN * CB_KROW];  // K codes, key-major
   uint8_t v[128 * CB_VROW];    // V codes, column-major (keys contiguous)
   uint32_t ks[CB_BN];          // the 4 E8M0 bytes of each key
-  uint8_t vs[2 * 128];         // E8M0 bytes of the two key blocks, per column
+  uint8_t vs[2 * 128];         // E8M0 bytes of the two key blocks: [block][c][dt] for column 32dt + c
 };
 
 __device__ __forceinline__ v8i make_v8i(uint4 a, uint4 b) {
@@ -64,54 +76,68 @@ __device__ __forceinline__ void swap32f(float& x, float& y) {
   y = __builtin_bit_cast(float, b);
 }
 
-// One thread's share of a tile load: two 16-byte K chunks, two 16-byte V chunks and, for threads
-// 0..127, one word of scales. Threads 0..63 fetch the 4 scale bytes of key tid, threads 64..127 one
-// word of the two V scale blocks.
-#define TILE_LOAD(k0, k1, v0, v1, sc, kt0)                                                            \
-  do {                                                                                                \
-    const uint8_t* ksrc_ = kc + (bhk * S + (kt0) + (tid >> 2)) * 128 + (tid & 3) * 32;                \
-    k0 = *reinterpret_cast<const uint4*>(ksrc_);                                                     \
-    k1 = *reinterpret_cast<const uint4*>(ksrc_ + 16);                                                \
-    const uint8_t* vsrc_ = vc + (bhk * 128 + (tid >> 1)) * S + (kt0) + (tid & 1) * 32;               \
-    v0 = *reinterpret_cast<const uint4*>(vsrc_);                                                     \
-    v1 = *reinterpret_cast<const uint4*>(vsrc_ + 16);                                                \
-    sc = (tid < 64) ? *reinterpret_cast<const uint32_t*>(ks + (bhk * S + (kt0) + (tid & 63)) * 4)    \
-                    : *reinterpret_cast<const uint32_t*>(vcs + (bhk * (S / 32) + (kt0) / 32) * 128 + \
-                                                         (tid & 63) * 4);                            \
+// One thread's share of a tile load: two 16-byte K chunks (key row tid/4), two 16-byte V chunks
+// (column tid/2) and one scale word: threads 0..63 the 4 E8M0 bytes of key tid, threads 64..127 one
+// word of the two V scale blocks (the other threads fetch a word they do not store).
+#define TILE_LOAD(k0, k1, v0, v1, sc, kt0)                                                             \
+  do {                                                                                                 \
+    const uint8_t* ksrc_ = kc + (bhk * S + (kt0) + (tid >> 2)) * 128 + (tid & 3) * 32;                 \
+    k0 = *reinterpret_cast<const uint4*>(ksrc_);                                                      \
+    k1 = *reinterpret_cast<const uint4*>(ksrc_ + 16);                                                 \
+    const uint8_t* vsrc_ = vc + (bhk * 128 + (tid >> 1)) * S + (kt0) + (tid & 1) * 32;                \
+    v0 = *reinterpret_cast<const uint4*>(vsrc_);                                                      \
+    v1 = *reinterpret_cast<const uint4*>(vsrc_ + 16);                                                 \
+    sc = (tid < 64) ? *reinterpret_cast<const uint32_t*>(ks + (bhk * S + (kt0) + (tid & 63)) * 4)     \
+                    : *reinterpret_cast<const uint32_t*>(vcs + (bhk * (S / 32) + (kt0) / 32) * 128 +  \
+                                                         (tid & 63) * 4);                             \
   } while (0)
+
+// LDS row of key kk (0..63) of a tile. Within a 32-key block, row 8g + 4h + j holds key
+// 16h + 4g + j: the score MFMA puts row 8(i/4) + 4hf + (i%4) into accumulator element i of lane
+// half hf, which is then key 16hf + i.
+__device__ __forceinline__ int k_lds_row(int kk) {
+  return (kk & 32) | (((kk >> 2) & 3) << 3) | (((kk >> 4) & 1) << 2) | (kk & 3);
+}
 
 __device__ __forceinline__ void store_tile(TileSmem& t, uint4 k0, uint4 k1, uint4 v0, uint4 v1, uint32_t sc,
                                            int tid) {
-  const int kr = tid >> 2, kch = (tid & 3) * 32;
+  const int kr = k_lds_row(tid >> 2), kch = (tid & 3) * 32;
   *reinterpret_cast<uint4*>(t.k + kr * CB_KROW + kch) = k0;
   *reinterpret_cast<uint4*>(t.k + kr * CB_KROW + kch + 16) = k1;
   const int d = tid >> 1, hv = (tid & 1) * 32;
   *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv) = v0;
   *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv + 16) = v1;
-  if (tid < 64)
-    t.ks[tid] = sc;
-  else if (tid < 128)
-    *reinterpret_cast<uint32_t*>(t.vs + (tid - 64) * 4) = sc;
+  if (tid < 64) {
+    t.ks[k_lds_row(tid)] = sc;
+  } else if (tid < 128) {
+    // the word holds columns d = 4w .. 4w+3 of block w / 32 (w = tid - 64); store column d = 32dt + c
+    // at [block][c][dt] so that one dword read gives a lane its four d-tiles' scales
+    const int w = tid - 64, blk = w >> 5, d0 = (w & 31) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int dd = d0 + e;
+      t.vs[blk * 128 + (dd & 31) * 4 + (dd >> 5)] = (uint8_t)(sc >> (8 * e));
+    }
+  }
 }
 
 // Per-wave running state of the online softmax.
 struct RowState {
   v16f o[4];   // O^T accumulator: lane (c, hf), element i of tile dt -> column 32dt + 8(i/4) + 4hf + i%4
-  float T;     // integer-valued running exponent
+  float T;     // integer-valued running exponent (set on the wave's first tile)
   float lsum;  // this lane's share of sum p
 };
 
-// One 64-key tile for one wave. kFull: both 32-key blocks are completed keys of this wave; otherwise
-// only the first block is (the second one's p is zero and its MFMA is skipped).
+// S^T = K Q^T for one 64-key tile (kFull) or its first 32-key block only. Lane (c, hf), element i of
+// sacc[kt] is the score of query c against key 32kt + 16hf + i (the K rows are permuted in LDS).
 template <bool kFull>
-__device__ __forceinline__ void process_tile(RowState& st, const TileSmem& t, const v8i (&qop)[2],
-                                             const int (&qsc)[2], float scale_log2, int c, int hf) {
-  // ---- S^T = K Q^T for the tile's 32-key blocks --------------------------------------------
-  v16f sacc[2];
+__device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const v8i (&qop)[2], const int (&qsc)[2],
+                                       int c, int hf) {
 #pragma unroll
-  for (int kt = 0; kt < (kFull ? 2 : 1); ++kt) {
+  for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+    if (kt == 1 && !kFull) continue;
     const uint32_t ksw = t.ks[32 * kt + c];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -121,83 +147,89 @@ __device__ __forceinline__ void process_tile(RowState& st, const TileSmem& t, co
       sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[m], sacc[kt], 0, 0, 0, ksc, 0, qsc[m]);
     }
   }
-  // Lane (c, hf), element i of block kt holds key 32kt + 8(i/4) + 4hf + (i%4) of the tile, query c.
+}
 
-  // ---- p = 2^(t - T) and the two block maxima ------------------------------------------------
-  float p[2][16];
-  float M0, M1;
-  for (int pass = 0; pass < 2; ++pass) {
-    const float negT = -st.T;
-    float pm0 = 0.f, pm1 = 0.f;
+// Softmax, P quantisation and O^T += V^T P^T for one tile whose scores are in sacc. kFull: both
+// 32-key blocks are completed keys of this wave; otherwise only the first one is (the second one's
+// p is zero).
+template <bool kFull>
+__device__ __forceinline__ void softmax_pv(RowState& st, const v16f (&sacc)[2], const TileSmem& t, float scale_log2,
+                                           int c, int hf, bool first) {
+  // Lane (c, hf), element i of block kt holds key 32kt + 16hf + i of the tile, query c.
+
+  // The V^T operands of this tile's P.V are read from LDS first, so their latency hides under the
+  // softmax below. Lane (c, hf), tile dt: column 32dt + c, keys 16hf + [0,16) and 32 + 16hf + [0,16).
+  v8i vop[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[0][i] = __builtin_amdgcn_exp2f(fmaf(sacc[0][i], scale_log2, negT));
-      pm0 = fmaxf(pm0, p[0][i]);
-      if (kFull) {
-        p[1][i] = __builtin_amdgcn_exp2f(fmaf(sacc[1][i], scale_log2, negT));
-        pm1 = fmaxf(pm1, p[1][i]);
-      } else {
-        p[1][i] = 0.f;
-      }
-    }
-    swap32f(pm0, pm1);  // lanes 0..31 now see both halves of block 0, lanes 32..63 of block 1
-    float mo = fmaxf(pm0, pm1), mo2 = mo;
-    swap32f(mo, mo2);  // every lane: mo = block-0 maximum, mo2 = block-1 maximum
-    M0 = mo;
-    M1 = mo2;
-    if (!__any(fmaxf(M0, M1) > CB_PMAX_LAZY)) break;
-    // Rare path: raise T to ceil(row max of t) and rescale by the exact power of two 2^(T - Tn).
-    float mt = -INFINITY;
+  for (int dt = 0; dt < 4; ++dt) {
+    const uint8_t* vr = t.v + (32 * dt + c) * CB_VROW + 16 * hf;
+    vop[dt] = make_v8i(*reinterpret_cast<const uint4*>(vr), *reinterpret_cast<const uint4*>(vr + 32));
+  }
+  const uint32_t vsw = *reinterpret_cast<const uint32_t*>(t.vs + hf * 128 + c * 4);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- block maxima of the raw scores, the lazy exponent, the E8M0 of each P block ------------
+  float m0 = sacc[0][0], m1 = kFull ? sacc[1][0] : -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mt = fmaxf(mt, sacc[0][i] * scale_log2);
-      if (kFull) mt = fmaxf(mt, sacc[1][i] * scale_log2);
-    }
-    float mt2 = mt;
-    swap32f(mt, mt2);
-    mt = fmaxf(mt, mt2);
-    const float Tn = fmaxf(st.T, ceilf(mt));
-    const float f = __builtin_amdgcn_exp2f(st.T - Tn);  // 0 on the first tile, else 2^-(integer)
+  for (int i = 1; i < 16; ++i) {
+    m0 = fmaxf(m0, sacc[0][i]);
+    if (kFull) m1 = fmaxf(m1, sacc[1][i]);
+  }
+  swap32f(m0, m1);  // lanes 0..31 now see both halves of block 0, lanes 32..63 of block 1
+  float M0 = fmaxf(m0, m1), M1 = M0;
+  swap32f(M0, M1);  // every lane: M0 = block-0 maximum, M1 = block-1 maximum (raw scores)
+  float negT = -st.T;
+  float pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
+  float pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
+  if (first || __any(fmaxf(pm0, pm1) > CB_PMAX_LAZY)) {
+    // Set T on a wave's first tile, and afterwards raise it when a block maximum of p would exceed
+    // 2^8: T += ceil(max (t - T)), rescaling O and l by the exact power of two 2^-shift.
+    const float shift = ceilf(fmaf(kFull ? fmaxf(M0, M1) : M0, scale_log2, negT));
+    const float f = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.o[dt][i] *= f;
     st.lsum *= f;
-    st.T = Tn;
+    st.T += shift;
+    negT = -st.T;
+    pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
+    pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) st.lsum += kFull ? p[0][i] + p[1][i] : p[0][i];
+  // Exponent -127 is only reached by blocks whose largest p is below 2^-118; they use -126, as the
+  // scale byte of the P operand must not be 0.
+  const int k0 = max(e8m0_exponent(pm0), -126), k1 = max(e8m0_exponent(pm1), -126);
+  const float nb0 = negT - (float)k0, nb1 = negT - (float)k1;
 
-  // ---- quantise P: one E8M0 per (query, 32-key block) --------------------------------------
-  // Exponent -127 is only reached by blocks whose largest p is below 2^-118; they use -126 so the
-  // conversion's power-of-two divisor stays a normal fp32 value.
-  const int k0 = max(e8m0_exponent(M0), -126), k1 = max(e8m0_exponent(M1), -126);
-  const float sc0 = u2f((uint32_t)(127 + k0) << 23), sc1 = u2f((uint32_t)(127 + k1) << 23);
-  uint32_t sl[8];
+  // ---- p / 2^k = 2^(t - T - k), its block sums and its E4M3 codes, four at a time ---------------
+  // Codes go straight into the B operand: lane (c, hf) bytes 4g..4g+3 are keys 16hf + 4g + [0,4) of
+  // block 0 and bytes 16 + 4g.. the same keys of block 1.
+  v8i pop;
+  float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    sl[g] = pack4_e4m3_scaled(p[0][4 * g], p[0][4 * g + 1], p[0][4 * g + 2], p[0][4 * g + 3], sc0);
-    sl[4 + g] = kFull ? pack4_e4m3_scaled(p[1][4 * g], p[1][4 * g + 1], p[1][4 * g + 2], p[1][4 * g + 3], sc1) : 0u;
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[0][4 * g + e], scale_log2, nb0));
+    ls0 += (q[0] + q[1]) + (q[2] + q[3]);
+    pop[g] = (int)pack4_e4m3(q[0], q[1], q[2], q[3]);
+    if (kFull) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[1][4 * g + e], scale_log2, nb1));
+      ls1 += (q[0] + q[1]) + (q[2] + q[3]);
+      pop[4 + g] = (int)pack4_e4m3(q[0], q[1], q[2], q[3]);
+    } else {
+      pop[4 + g] = 0;
+    }
   }
-  // Slot g holds keys 8g + 4hf + [0,4) of its block. The B operand of O^T wants, in lane hf,
-  // keys 16hf + [0,16) of block 0 then of block 1: trade slots 2,3 (6,7) of the lower half for
-  // slots 0,1 (4,5) of the upper half.
-  swap32(sl[0], sl[2]);
-  swap32(sl[1], sl[3]);
-  swap32(sl[4], sl[6]);
-  swap32(sl[5], sl[7]);
-  v8i pop;
-  pop[0] = (int)sl[0]; pop[1] = (int)sl[2]; pop[2] = (int)sl[1]; pop[3] = (int)sl[3];
-  pop[4] = (int)sl[4]; pop[5] = (int)sl[6]; pop[6] = (int)sl[5]; pop[7] = (int)sl[7];
+  st.lsum += kFull ? ldexpf(ls0, k0) + ldexpf(ls1, k1) : ldexpf(ls0, k0);
   const int psc = (hf ? k1 : k0) + 127;
 
   // ---- O^T += V^T P^T over the four 32-column tiles of D -----------------------------------
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    const uint8_t* vr = t.v + (32 * dt + c) * CB_VROW + 16 * hf;
-    const v8i vop = make_v8i(*reinterpret_cast<const uint4*>(vr), *reinterpret_cast<const uint4*>(vr + 32));
-    const int vsc = t.vs[hf * 128 + 32 * dt + c];
-    st.o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, st.o[dt], 0, 0, 0, vsc, 0, psc);
+    const int vsc = (int)((vsw >> (8 * dt)) & 0xffu);
+    st.o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[dt], pop, st.o[dt], 0, 0, 0, vsc, 0, psc);
   }
 }
 
@@ -205,6 +237,8 @@ struct AttnParams {
   const uint8_t *qc, *qs, *kc, *ks, *vc, *vcs;  // rowwise Q/K and columnwise V codes/scales
   const uint8_t *vt, *vta;                       // token-normalised V (fused epilogue only)
   int S, Hq, Hkv, n_qtiles;
+  int n_pairs;                                   // B * Hq
+  int xcd_pairs;                                 // n_pairs / 8 when n_pairs % 8 == 0, else 0
   float scale_log2;                              // softmax_scale * log2(e)
   float *o_c, *lse_c;                            // completed partial (unfused)
   void* out;                                     // final output view (fused)
@@ -214,16 +248,17 @@ struct AttnParams {
 };
 
 // LDS: the double-buffered K/V tiles of the main loop, reused afterwards (fused epilogue) for each
-// wave's decoded token-normalised own-block V, 32 keys x 128 columns of fp32.
-constexpr int CB_LDS_BYTES = 4 * 32 * 128 * 4;
-static_assert(2 * sizeof(TileSmem) <= CB_LDS_BYTES, "tile buffers must fit the LDS block");
+// wave's decoded token-normalised own-block V, 32 keys x 128 columns of bf16 (exact: E4M3 values times
+// a power of two need 4 significant bits).
+constexpr int CB_LDS_BYTES = 2 * sizeof(TileSmem);
+static_assert(4 * 32 * 128 * 2 <= CB_LDS_BYTES, "the own-block V must fit the tile buffers");
 
 // kFused = false: the completed-block partial (O_c, lse_c). kFused = true: the whole attention of
 // the row: completed blocks, the own block on the token-normalised V (TE#3865 Description, second
 // bullet), and the merge through the log-sum-exps, written once in the output's layout.
 template <bool kFused>
 __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
-  __shared__ __align__(16) uint8_t lds[kFused ? CB_LDS_BYTES : 2 * sizeof(TileSmem)];
+  __shared__ __align__(16) uint8_t lds[CB_LDS_BYTES];
   TileSmem* sm = reinterpret_cast<TileSmem*>(lds);  // sm[0], sm[1]
   const int S = P.S;
   const uint8_t *__restrict__ kc = P.kc, *__restrict__ ks = P.ks, *__restrict__ vc = P.vc,
@@ -231,8 +266,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   const float scale_log2 = P.scale_log2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hf = lane >> 5;
-  const int qtile = P.n_qtiles - 1 - (int)blockIdx.x;  // longest first
-  const int hq = blockIdx.y, b = blockIdx.z;
+  // Workgroup id -> (query tile, pair): round r = id / n_pairs takes query tile n_qtiles - 1 - r; the
+  // pair index within the round is permuted so that the ids one XCD receives (id mod 8 equal) cover
+  // n_pairs / 8 adjacent pairs.
+  const int id = (int)blockIdx.x;
+  const int round = id / P.n_pairs, slot = id - round * P.n_pairs;
+  const int qtile = P.n_qtiles - 1 - round;
+  const int pair = P.xcd_pairs ? (slot & 7) * P.xcd_pairs + (slot >> 3) : slot;
+  const int b = pair / P.Hq, hq = pair - b * P.Hq;
   const int hk = hq / (P.Hq / P.Hkv);
   const int q0 = qtile * CB_BM;
   const int qw = q0 + 32 * wave;          // first query of this wave; its completed keys are j < qw
@@ -263,9 +304,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) st.o[dt][i] = 0.f;
-  st.T = -INFINITY;
+  st.T = 0.f;
   st.lsum = 0.f;
 
+  // Tile it of the workgroup's key range is full for this wave when 64(it+1) <= e_w, half (first
+  // 32-key block only) when 64it < e_w < 64(it+1), and outside the wave's range when 64it >= e_w.
   uint4 pk0, pk1, pv0, pv1;
   uint32_t psc;
   if (ntiles > 0) {
@@ -279,10 +322,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
     const int kn = (it + 1 < ntiles) ? kt0 + CB_BN : kt0;
     TILE_LOAD(pk0, pk1, pv0, pv1, psc, kn);
     const TileSmem& cur = sm[it & 1];
-    if (kt0 + CB_BN <= e_w)
-      process_tile<true>(st, cur, qop, qsc, scale_log2, c, hf);
-    else if (kt0 < e_w)
-      process_tile<false>(st, cur, qop, qsc, scale_log2, c, hf);
+    v16f sacc[2];
+    if (kt0 + CB_BN <= e_w) {
+      scores<true>(sacc, cur, qop, qsc, c, hf);
+      softmax_pv<true>(st, sacc, cur, scale_log2, c, hf, it == 0);
+    } else if (kt0 < e_w) {
+      scores<false>(sacc, cur, qop, qsc, c, hf);
+      softmax_pv<false>(st, sacc, cur, scale_log2, c, hf, it == 0);
+    }
     if (it + 1 < ntiles) store_tile(sm[(it + 1) & 1], pk0, pk1, pv0, pv1, psc, tid);
     __syncthreads();
   }
@@ -309,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
     return;
   } else {
     // ---- own block: keys qw .. qw+31, query qw + c sees keys up to itself ----------------------
-    float* vown = reinterpret_cast<float*>(lds) + wave * (32 * 128);  // this wave's 32 x 128 fp32
+    uint16_t* vown = reinterpret_cast<uint16_t*>(lds) + wave * (32 * 128);  // this wave's 32 x 128 bf16
     v16f so;
 #pragma unroll
     for (int i = 0; i < 16; ++i) so[i] = 0.f;
@@ -332,12 +379,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
       for (int q = 0; q < 4; ++q) {
         const uint4 w = *reinterpret_cast<const uint4*>(vrow + 16 * q);
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        uint32_t packed[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float4 f = make_float4(e4m3_to_f32(ww[r] & 0xffu) * amp, e4m3_to_f32((ww[r] >> 8) & 0xffu) * amp,
-                                       e4m3_to_f32((ww[r] >> 16) & 0xffu) * amp, e4m3_to_f32(ww[r] >> 24) * amp);
-          *reinterpret_cast<float4*>(vown + j * 128 + d0 + 16 * q + 4 * r) = f;
+          // E4M3 value times 2^amp has at most 4 significant bits: its top 16 bits are the exact bf16
+          const uint32_t b0 = f2u(e4m3_to_f32(ww[r] & 0xffu) * amp) >> 16;
+          const uint32_t b1 = f2u(e4m3_to_f32((ww[r] >> 8) & 0xffu) * amp) >> 16;
+          const uint32_t b2 = f2u(e4m3_to_f32((ww[r] >> 16) & 0xffu) * amp) >> 16;
+          const uint32_t b3 = f2u(e4m3_to_f32(ww[r] >> 24) * amp) >> 16;
+          packed[2 * r] = b0 | (b1 << 16);
+          packed[2 * r + 1] = b2 | (b3 << 16);
         }
+        uint4* dst = reinterpret_cast<uint4*>(vown + j * 128 + d0 + 16 * q);
+        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
       }
     }
     __syncthreads();  // decoded rows visible to the whole wave
@@ -386,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int j = 8 * (u >> 2) + 4 * hf + (u & 3);
-        const float a = vown[j * 128 + 32 * dt + c];
+        const float a = u2f((uint32_t)vown[j * 128 + 32 * dt + c] << 16);
         oo = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pa[u], oo, 0, 0, 0);
       }
 #pragma unroll
@@ -410,11 +465,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
 }
 
 static AttnParams base_params(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                              const uint8_t* vc, const uint8_t* vcs, int S, int Hq, int Hkv, float softmax_scale) {
+                              const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv,
+                              float softmax_scale) {
   AttnParams p{};
   p.qc = qc; p.qs = qs; p.kc = kc; p.ks = ks; p.vc = vc; p.vcs = vcs;
   p.S = S; p.Hq = Hq; p.Hkv = Hkv;
   p.n_qtiles = (S + CB_BM - 1) / CB_BM;
+  p.n_pairs = B * Hq;
+  p.xcd_pairs = (p.n_pairs % 8 == 0) ? p.n_pairs / 8 : 0;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   return p;
 }
@@ -422,10 +480,10 @@ static AttnParams base_params(const uint8_t* qc, const uint8_t* qs, const uint8_
 hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                  const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv,
                                  float softmax_scale, float* o_c, float* lse_c, hipStream_t stream) {
-  AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, S, Hq, Hkv, softmax_scale);
+  AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, B, S, Hq, Hkv, softmax_scale);
   p.o_c = o_c;
   p.lse_c = lse_c;
-  attn_kernel<false><<<dim3((unsigned)p.n_qtiles, (unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(p);
+  attn_kernel<false><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -433,7 +491,7 @@ hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t
                              const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B,
                              int S, int Hq, int Hkv, float softmax_scale, void* out, int64_t osb, int64_t oss,
                              int64_t osh, int out_bf16, float* lse_out, hipStream_t stream) {
-  AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, S, Hq, Hkv, softmax_scale);
+  AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, B, S, Hq, Hkv, softmax_scale);
   p.vt = vt;
   p.vta = vta;
   p.out = out;
@@ -442,7 +500,7 @@ hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t
   p.osh = osh;
   p.out_bf16 = out_bf16;
   p.lse_out = lse_out;
-  attn_kernel<true><<<dim3((unsigned)p.n_qtiles, (unsigned)Hq, (unsigned)B), dim3(256), 0, stream>>>(p);
+  attn_kernel<true><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 
