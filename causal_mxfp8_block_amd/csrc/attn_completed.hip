@@ -47,11 +47,12 @@ constexpr int CB_BN = 64;     // keys per tile (two 32-key MX blocks)
 constexpr int CB_KROW = 144;  // LDS bytes per K row (128 codes + 16 pad: conflict-free 16-byte reads)
 constexpr int CB_VROW = 80;   // LDS bytes per V column (64 codes + 16 pad)
 constexpr float CB_PMAX_LAZY = 256.0f;  // raise T once a block maximum of p exceeds 2^8
+constexpr int CB_RSRC_W3 = 0x00020000;  // buffer descriptor word 3 on gfx9: 32-bit data, raw offsets
 
 struct __align__(16) TileSmem {
   uint8_t k[CB_BN * CB_KROW];  // K codes, key-major
   uint8_t v[128 * CB_VROW];    // V codes, column-major (keys contiguous)
-  uint32_t ks[CB_BN];          // the 4 E8M0 bytes of each key
+  uint32_t ks[CB_BN];          // the 4 E8M0 bytes of each key, stored in the byte order s0 s2 s1 s3
   uint8_t vs[2 * 128];         // E8M0 bytes of the two key blocks: [block][c][dt] for column 32dt + c
 };
 
@@ -60,6 +61,31 @@ __device__ __forceinline__ v8i make_v8i(uint4 a, uint4 b) {
   r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
   r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
   return r;
+}
+
+// IEEE 754-2019 maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no NaN quieting of
+// MFMA results first. Every input here is finite.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// A VGPR whose previous contents do not matter: the empty asm defines it without an instruction, so
+// packing four codes does not first clear the half-word the second conversion fills.
+__device__ __forceinline__ int fresh_reg() {
+  int u;
+  asm volatile("" : "=v"(u));
+  return u;
+}
+
+// E4M3 codes of four fp32 values (round to nearest even; every value here is at most 464, which
+// converts to 448), a in the lowest byte.
+__device__ __forceinline__ int pack4_p(float a, float b, float c, float d) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, fresh_reg(), false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Block-scaled FP8 MFMA whose A and B scales are byte kSelA / kSelB of the scale registers.
+template <int kSelA, int kSelB>
+__device__ __forceinline__ v16f mfma_mx(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, kSelA, sa, kSelB, sb);
 }
 
 // Exchange with lane ^ 32 (v_permlane32_swap): afterwards x holds, in lanes 32..63, what y held in
@@ -76,25 +102,23 @@ __device__ __forceinline__ void swap32f(float& x, float& y) {
   y = __builtin_bit_cast(float, b);
 }
 
-// One thread's share of a tile load: two 16-byte K chunks (key row tid/4), two 16-byte V chunks
-// (column tid/2) and one scale word: threads 0..63 the 4 E8M0 bytes of key tid, threads 64..127 one
-// word of the two V scale blocks (the other threads fetch a word they do not store).
-#define TILE_LOAD(k0, k1, v0, v1, sc, kt0)                                                             \
-  do {                                                                                                 \
-    const uint8_t* ksrc_ = kc + (bhk * S + (kt0) + (tid >> 2)) * 128 + (tid & 3) * 32;                 \
-    k0 = *reinterpret_cast<const uint4*>(ksrc_);                                                      \
-    k1 = *reinterpret_cast<const uint4*>(ksrc_ + 16);                                                 \
-    const uint8_t* vsrc_ = vc + (bhk * 128 + (tid >> 1)) * S + (kt0) + (tid & 1) * 32;                \
-    v0 = *reinterpret_cast<const uint4*>(vsrc_);                                                      \
-    v1 = *reinterpret_cast<const uint4*>(vsrc_ + 16);                                                 \
-    sc = (tid < 64) ? *reinterpret_cast<const uint32_t*>(ks + (bhk * S + (kt0) + (tid & 63)) * 4)     \
-                    : *reinterpret_cast<const uint32_t*>(vcs + (bhk * (S / 32) + (kt0) / 32) * 128 +  \
-                                                         (tid & 63) * 4);                             \
+// One thread's share of a tile load, through buffer resources over the current (b, kv-head) slice:
+// two 16-byte K chunks (key row tid/4 at byte offset kvoff), two 16-byte V chunks (column tid/2 at
+// byte offset vvoff) and, in waves 0 and 1, one scale word: wave 0 the 4 E8M0 bytes of key tid, wave
+// 1 one word of the tile's two V scale blocks. The per-tile offset is a scalar.
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+#define TILE_LOAD(k0, k1, v0, v1, sc, kt0)                                           \
+  do {                                                                               \
+    k0 = bload16(rk, kvoff, (kt0) * 128);                                            \
+    k1 = bload16(rk, kvoff + 16, (kt0) * 128);                                       \
+    v0 = bload16(rv, vvoff, (kt0));                                                  \
+    v1 = bload16(rv, vvoff + 16, (kt0));                                             \
+    if (wave_u < 2)                                                                  \
+      sc = __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, wave_u == 0 ? (kt0) * 4 : ((kt0) >> 5) * 128, 0); \
   } while (0)
 
-// LDS row of key kk (0..63) of a tile. Within a 32-key block, row 8g + 4h + j holds key
-// 16h + 4g + j: the score MFMA puts row 8(i/4) + 4hf + (i%4) into accumulator element i of lane
-// half hf, which is then key 16hf + i.
 __device__ __forceinline__ int k_lds_row(int kk) {
   return (kk & 32) | (((kk >> 2) & 3) << 3) | (((kk >> 4) & 1) << 2) | (kk & 3);
 }
@@ -108,7 +132,8 @@ __device__ __forceinline__ void store_tile(TileSmem& t, uint4 k0, uint4 k1, uint
   *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv) = v0;
   *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv + 16) = v1;
   if (tid < 64) {
-    t.ks[k_lds_row(tid)] = sc;
+    // bytes s0 s2 s1 s3: the 16-bit half hf then holds the scales of D-blocks hf and 2 + hf
+    t.ks[k_lds_row(tid)] = __builtin_amdgcn_perm(sc, sc, 0x03010200u);
   } else if (tid < 128) {
     // the word holds columns d = 4w .. 4w+3 of block w / 32 (w = tid - 64); store column d = 32dt + c
     // at [block][c][dt] so that one dword read gives a lane its four d-tiles' scales
@@ -133,20 +158,30 @@ struct RowState {
 template <bool kFull>
 __device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const v8i (&qop)[2], const int (&qsc)[2],
                                        int c, int hf) {
+  constexpr int nkt = kFull ? 2 : 1;
+  // All K operands first, so the LDS round trips overlap. Lane (c, hf) supplies row c of each 32-key
+  // block: bytes d = 64m + 16hf + [0,16) and 64m + 32 + 16hf + [0,16); its scale for step m is byte m
+  // of the 16-bit half hf of the row's permuted scale word.
+  v8i kop[nkt][2];
+  int ksc[nkt];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < nkt; ++kt) {
+    const uint8_t* kr = t.k + (32 * kt + c) * CB_KROW + 16 * hf;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      kop[kt][m] = make_v8i(*reinterpret_cast<const uint4*>(kr + 64 * m),
+                            *reinterpret_cast<const uint4*>(kr + 64 * m + 32));
+    ksc[kt] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(t.ks) + (32 * kt + c) * 4 + 2 * hf);
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
-    if (kt == 1 && !kFull) continue;
-    const uint32_t ksw = t.ks[32 * kt + c];
+  // Independent accumulators alternate, so no MFMA waits on the one just issued.
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const uint8_t* kr = t.k + (32 * kt + c) * CB_KROW + 64 * m + 16 * hf;
-      const v8i kop = make_v8i(*reinterpret_cast<const uint4*>(kr), *reinterpret_cast<const uint4*>(kr + 32));
-      const int ksc = (int)((ksw >> (8 * (2 * m + hf))) & 0xffu);
-      sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[m], sacc[kt], 0, 0, 0, ksc, 0, qsc[m]);
-    }
-  }
+  for (int kt = 0; kt < nkt; ++kt) sacc[kt] = mfma_mx<0, 0>(kop[kt][0], qop[0], sacc[kt], ksc[kt], qsc[0]);
+#pragma unroll
+  for (int kt = 0; kt < nkt; ++kt) sacc[kt] = mfma_mx<1, 0>(kop[kt][1], qop[1], sacc[kt], ksc[kt], qsc[1]);
 }
 
 // Softmax, P quantisation and O^T += V^T P^T for one tile whose scores are in sacc. kFull: both
@@ -172,19 +207,19 @@ __device__ __forceinline__ void softmax_pv(RowState& st, const v16f (&sacc)[2], 
   float m0 = sacc[0][0], m1 = kFull ? sacc[1][0] : -INFINITY;
 #pragma unroll
   for (int i = 1; i < 16; ++i) {
-    m0 = fmaxf(m0, sacc[0][i]);
-    if (kFull) m1 = fmaxf(m1, sacc[1][i]);
+    m0 = vmax(m0, sacc[0][i]);
+    if (kFull) m1 = vmax(m1, sacc[1][i]);
   }
   swap32f(m0, m1);  // lanes 0..31 now see both halves of block 0, lanes 32..63 of block 1
-  float M0 = fmaxf(m0, m1), M1 = M0;
+  float M0 = vmax(m0, m1), M1 = M0;
   swap32f(M0, M1);  // every lane: M0 = block-0 maximum, M1 = block-1 maximum (raw scores)
   float negT = -st.T;
   float pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
   float pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
-  if (first || __any(fmaxf(pm0, pm1) > CB_PMAX_LAZY)) {
+  if (first || __any(vmax(pm0, pm1) > CB_PMAX_LAZY)) {
     // Set T on a wave's first tile, and afterwards raise it when a block maximum of p would exceed
     // 2^8: T += ceil(max (t - T)), rescaling O and l by the exact power of two 2^-shift.
-    const float shift = ceilf(fmaf(kFull ? fmaxf(M0, M1) : M0, scale_log2, negT));
+    const float shift = ceilf(fmaf(kFull ? vmax(M0, M1) : M0, scale_log2, negT));
     const float f = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -196,10 +231,14 @@ __device__ __forceinline__ void softmax_pv(RowState& st, const v16f (&sacc)[2], 
     pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
     pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
   }
-  // Exponent -127 is only reached by blocks whose largest p is below 2^-118; they use -126, as the
+  // E8M0 byte 127 + k of each P block: k = E - 8, plus 1 when the mantissa of the block maximum
+  // exceeds 1.75 (adding 2^21 - 1 to the bits carries into the exponent exactly then). Exponent
+  // -127 (byte 0) is only reached by blocks whose largest p is below 2^-118; they use byte 1, as the
   // scale byte of the P operand must not be 0.
-  const int k0 = max(e8m0_exponent(pm0), -126), k1 = max(e8m0_exponent(pm1), -126);
-  const float nb0 = negT - (float)k0, nb1 = negT - (float)k1;
+  const int e0 = max((int)((f2u(pm0) + 0x1FFFFFu) >> 23), 9) - 8;
+  const int e1 = kFull ? max((int)((f2u(pm1) + 0x1FFFFFu) >> 23), 9) - 8 : 1;
+  const float t127 = 127.f - st.T;
+  const float nb0 = t127 - (float)e0, nb1 = t127 - (float)e1;  // -T - k of each block
 
   // ---- p / 2^k = 2^(t - T - k), its block sums and its E4M3 codes, four at a time ---------------
   // Codes go straight into the B operand: lane (c, hf) bytes 4g..4g+3 are keys 16hf + 4g + [0,4) of
@@ -212,25 +251,24 @@ __device__ __forceinline__ void softmax_pv(RowState& st, const v16f (&sacc)[2], 
 #pragma unroll
     for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[0][4 * g + e], scale_log2, nb0));
     ls0 += (q[0] + q[1]) + (q[2] + q[3]);
-    pop[g] = (int)pack4_e4m3(q[0], q[1], q[2], q[3]);
+    pop[g] = pack4_p(q[0], q[1], q[2], q[3]);
     if (kFull) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[1][4 * g + e], scale_log2, nb1));
       ls1 += (q[0] + q[1]) + (q[2] + q[3]);
-      pop[4 + g] = (int)pack4_e4m3(q[0], q[1], q[2], q[3]);
+      pop[4 + g] = pack4_p(q[0], q[1], q[2], q[3]);
     } else {
       pop[4 + g] = 0;
     }
   }
-  st.lsum += kFull ? ldexpf(ls0, k0) + ldexpf(ls1, k1) : ldexpf(ls0, k0);
-  const int psc = (hf ? k1 : k0) + 127;
+  st.lsum += kFull ? ldexpf(ls0, e0 - 127) + ldexpf(ls1, e1 - 127) : ldexpf(ls0, e0 - 127);
+  const int psc = hf ? e1 : e0;
 
-  // ---- O^T += V^T P^T over the four 32-column tiles of D -----------------------------------
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const int vsc = (int)((vsw >> (8 * dt)) & 0xffu);
-    st.o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[dt], pop, st.o[dt], 0, 0, 0, vsc, 0, psc);
-  }
+  // ---- O^T += V^T P^T over the four 32-column tiles of D (V scale: byte dt of vsw) ------------
+  st.o[0] = mfma_mx<0, 0>(vop[0], pop, st.o[0], (int)vsw, psc);
+  st.o[1] = mfma_mx<1, 0>(vop[1], pop, st.o[1], (int)vsw, psc);
+  st.o[2] = mfma_mx<2, 0>(vop[2], pop, st.o[2], (int)vsw, psc);
+  st.o[3] = mfma_mx<3, 0>(vop[3], pop, st.o[3], (int)vsw, psc);
 }
 
 struct AttnParams {
@@ -265,6 +303,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
                 *__restrict__ vcs = P.vcs;
   const float scale_log2 = P.scale_log2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same, as a scalar (tile loads only)
   const int c = lane & 31, hf = lane >> 5;
   // Workgroup id -> (query tile, pair): round r = id / n_pairs takes query tile n_qtiles - 1 - r; the
   // pair index within the round is permuted so that the ids one XCD receives (id mod 8 equal) cover
@@ -282,6 +321,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   const int e_wg = min(q0 + 96, S - 32);  // key range end of the last valid wave
   const int ntiles = (e_wg + CB_BN - 1) / CB_BN;
   const int64_t bhq = (int64_t)b * P.Hq + hq, bhk = (int64_t)b * P.Hkv + hk;
+  // Buffer resources over this kv head's K codes [S,128], V codes [128,S] and K or V scales.
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kc + bhk * S * 128), 0, S * 128, CB_RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vc + bhk * S * 128), 0, S * 128, CB_RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rs =
+      wave_u == 0 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ks + bhk * S * 4), 0, S * 4, CB_RSRC_W3)
+                : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vcs + bhk * S * 4), 0, S * 4, CB_RSRC_W3);
+  const int kvoff = (tid >> 2) * 128 + (tid & 3) * 32, vvoff = (tid >> 1) * S + (tid & 1) * 32,
+            svoff = (tid & 63) * 4;
 
   // Q^T operand (B of S^T = K Q^T) for the two 64-wide K steps over D. Lane (c, hf) holds bytes
   // d = 64m + 16hf + [0,16) and 64m + 32 + 16hf + [0,16) of query qw + c; its scale is that of
@@ -310,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   // Tile it of the workgroup's key range is full for this wave when 64(it+1) <= e_w, half (first
   // 32-key block only) when 64it < e_w < 64(it+1), and outside the wave's range when 64it >= e_w.
   uint4 pk0, pk1, pv0, pv1;
-  uint32_t psc;
+  uint32_t psc = 0;
   if (ntiles > 0) {
     TILE_LOAD(pk0, pk1, pv0, pv1, psc, 0);
     store_tile(sm[0], pk0, pk1, pv0, pv1, psc, tid);
