@@ -88,8 +88,8 @@ def cpu_baseline(inp, rows_n: int, seed: int = 0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa16x4_s32k_amplitudes")
     ap.add_argument("--path", choices=["fused", "stepwise"], default="fused")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle CPU-baseline sample (0 skips)")

@@ -206,3 +206,33 @@ def test_gqa_equals_repeated_kv():
     o2, l2 = mx.attn_fwd(q, k4, v4, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_accuracy_against_unquantized(name):
+    """Accuracy report (printed as one ACCURACY line per workload): on the sampled rows, max|err|/RMS
+    and RMS(err)/RMS of (i) the GPU leak-free forward vs the oracle, (ii) the GPU leak-free forward vs
+    the fp64 unquantised causal attention on the same bf16 inputs, (iii) the oracle's ordinary
+    (leaky) causal MXFP8 forward vs that same reference. RMS is that of the unquantised output. The
+    MXFP8 error against the unquantised reference is quantisation error, so (ii) is only checked to
+    be of the size of the leaky variant's (iii), not against a tolerance."""
+    inp = make_inputs(name)
+    w = inp.workload
+    say(f"accuracy {name}")
+    go, _ = gpu_forward(inp, torch.float32)
+    rows = None if w.S <= 1024 else sample_rows(w.S, w.seed)
+    q, k, v = oracle_view(inp, "q"), oracle_view(inp, "k"), oracle_view(inp, "v")
+    z = _oracle_quant(inp)
+    ro, _, _ = oracle.forward(q, k, v, w.scale, rows, quant=z)
+    rr, _ = oracle.attn_reference(q, k, v, w.scale, rows)
+    rl, _ = oracle.forward_leaky(q, k, v, w.scale, rows, quant=z)
+    rms = np.sqrt(np.mean(rr ** 2)) if rows is None else \
+        np.sqrt(np.mean(oracle.attn_reference(q, k, v, w.scale, uniform_rows(w.S, w.seed))[0] ** 2))
+    sel = slice(None) if rows is None else rows
+    g = go[:, :, sel]
+    fig = lambda e: (np.max(np.abs(e)) / rms, np.sqrt(np.mean(e ** 2)) / rms)
+    e1, e2, e3 = fig(g - ro), fig(g - rr), fig(rl - rr)
+    say(f"ACCURACY {name} rows={'all' if rows is None else len(rows)} rms_ref={rms:.4e} | "
+        f"gpu-vs-oracle max {e1[0]:.3e} rms {e1[1]:.3e} | gpu-vs-unquantised max {e2[0]:.3e} rms {e2[1]:.3e} | "
+        f"leaky-oracle-vs-unquantised max {e3[0]:.3e} rms {e3[1]:.3e}")
+    assert e2[1] <= 2.0 * e3[1] + 1e-3
