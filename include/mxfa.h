@@ -17,8 +17,8 @@
  *   - Every call validates its arguments on the host first. On any error it returns a nonzero
  *     mxfa_status, enqueues nothing, and mxfa_last_error() names the violated constraint. There is
  *     no slower fallback path for unsupported shapes.
- *   - Supported shapes: D == 128, S % 32 == 0, B, S, H >= 1, Hq % Hkv == 0 (GQA: q-head hq reads
- *     kv-head hq / (Hq/Hkv)), equal query and key lengths, causal.
+ *   - Supported shapes: D == 128, S % 32 == 0, 1 <= S <= 2^24, B, H >= 1, Hq % Hkv == 0 (GQA: q-head
+ *     hq reads kv-head hq / (Hq/Hkv)), equal query and key lengths, causal.
  *   - bf16 tensors are addressed by element strides (sb, ss, sh) of a logical [B,S,H,D] tensor with
  *     unit stride along D (BSHD and SBHD are both such views). Pointers must be 16-byte aligned and
  *     bf16 strides multiples of 8 elements.
