@@ -347,6 +347,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
       qsc[m] = (int)((sw >> (8 * (2 * m + hf))) & 0xffu);
     }
   }
+  // Wait for Q here (vmcnt 0, other counters untouched). Otherwise the loop's first use of Q carries
+  // a conservative vector-memory wait that also waits for the tile prefetch issued just before it,
+  // exposing the global-memory latency on every tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   RowState st;
 #pragma unroll
@@ -380,6 +384,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
       softmax_pv<false>(st, sacc, cur, scale_log2, c, hf, it == 0);
     }
     if (it + 1 < ntiles) store_tile(sm[(it + 1) & 1], pk0, pk1, pv0, pv1, psc, tid);
+    // Unconditional vmcnt(0): the prefetch is complete on every path out of the iteration (the
+    // store above already needs it except on the last one). Without it the compiler must assume the
+    // prefetch registers may still be in flight at the top of the next iteration, and makes the
+    // first score MFMA wait for the new tile's loads, exposing their latency on every tile.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
