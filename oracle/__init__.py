@@ -54,7 +54,7 @@ def _load():
         six = [P] * 6
         lib.orc_attn_completed.argtypes = six + [I, I, I, I, I, F, P, I, I, P, P, D, P, P, D, ctypes.c_uint64]
         lib.orc_attn_own.argtypes = six + [I, I, I, I, I, F, P, I, P, P, D, P, P, D, ctypes.c_uint64]
-        lib.orc_attn_leaky.argtypes = six + [I, I, I, I, I, F, P, I, P, P]
+        lib.orc_attn_leaky.argtypes = six + [I, I, I, I, I, F, P, I, P, P, D, P, P, D, ctypes.c_uint64]
         lib.orc_lse_merge.argtypes = [P, P, P, P, I64, I, P, P]
         raw = [P, I64, I64, I64] * 3
         lib.orc_attn_reference.argtypes = raw + [I, I, I, I, I, F, P, I, P, P]
@@ -208,14 +208,19 @@ def attn_own(qc, qs, kc, ks, vt, vta, Hq, Hkv, scale, rows=None, allowance=False
     return (o, lse, al, le) if allowance else (o, lse)
 
 
-def attn_leaky(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None):
-    """Ordinary causal MXFP8 (keys j <= i through the completed-block machinery)."""
+def attn_leaky(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None, allowance=False, score_err=SCORE_ERR, jitter=0.0,
+               jitter_seed=0):
+    """Ordinary causal MXFP8 (keys j <= i through the completed-block machinery, the last P block
+    partial). ``allowance``, ``score_err``, ``jitter``: as for attn_completed."""
     B, _, S, D = qc.shape
     r, n = _rows_arg(rows, S)
     o, lse = _out(B, Hq, n, D)
+    al = np.empty_like(o) if allowance else None
+    le = np.empty_like(lse) if allowance else None
     args = [np.ascontiguousarray(a) for a in (qc, qs, kc, ks, vc, vcs)]
-    _load().orc_attn_leaky(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, _ptr(o), _ptr(lse))
-    return o, lse
+    _load().orc_attn_leaky(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, _ptr(o), _ptr(lse),
+                           float(score_err), _ptr(al), _ptr(le), float(jitter), int(jitter_seed))
+    return (o, lse, al, le) if allowance else (o, lse)
 
 
 def lse_merge(oc, lsec, oo, lseo):
@@ -289,8 +294,9 @@ def forward(q, k, v, scale, rows=None, quant: Quantized | None = None, score_err
                     "allowance_o": alo, "allowance": al, "lse_err": wc * ec + wo * eo}
 
 
-def forward_leaky(q, k, v, scale, rows=None, quant: Quantized | None = None):
-    """Ordinary causal MXFP8 forward (the variant that leaks through V scales)."""
+def forward_leaky(q, k, v, scale, rows=None, quant: Quantized | None = None, allowance=False):
+    """Ordinary causal MXFP8 forward (the variant that leaks through V scales); with ``allowance``
+    also the R15 allowance and lse error bound, as attn_leaky."""
     qv, kv = _as_view(q), _as_view(k)
     z = quant if quant is not None else quantize_all(q, k, v)
-    return attn_leaky(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, qv.H, kv.H, scale, rows)
+    return attn_leaky(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, qv.H, kv.H, scale, rows, allowance=allowance)

@@ -491,11 +491,13 @@ void orc_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
 
 void orc_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
                     const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
-                    int nrows, double* o, double* lse) {
+                    int nrows, double* o, double* lse, double score_err, double* allowance, double* lse_err,
+                    double jitter, uint64_t jitter_seed) {
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vcol(vc, vcs, B, Hkv, S, D);
-  run_rows(PART_LEAKY, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, 0, 0.0, 0.0, 0, o, lse, NULL, NULL);
+  run_rows(PART_LEAKY, Q, K, V, B, S, Hq, Hkv, D, scale, rows, nrows, 1, 0, score_err, jitter, jitter_seed, o, lse,
+           allowance, lse_err);
   free(Q);
   free(K);
   free(V);

@@ -74,10 +74,13 @@ void orc_lse_merge(const double* oc, const double* lsec, const double* oo, const
                    double* o, double* lse);
 
 /* Ordinary ("leaky") causal MXFP8: every key j <= i through the O7 machinery
-   with the columnwise V, whose own-block scale also covers future tokens. */
+   with the columnwise V, whose own-block scale also covers future tokens; the
+   last P block is partial (its E8M0 from the visible keys only). allowance,
+   lse_err, score_err, jitter: as for orc_attn_completed (may be NULL / 0). */
 void orc_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
                     const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D, float scale, const int32_t* rows,
-                    int nrows, double* o, double* lse);
+                    int nrows, double* o, double* lse, double score_err, double* allowance, double* lse_err,
+                    double jitter, uint64_t jitter_seed);
 /* Unquantised textbook causal softmax attention on the bf16 values. */
 void orc_attn_reference(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh, const uint16_t* k, int64_t ksb,
                         int64_t kss, int64_t ksh, const uint16_t* v, int64_t vsb, int64_t vss, int64_t vsh, int B,

@@ -232,3 +232,22 @@ def test_merged_allowance_covers_score_error():
         oo, lo = oracle.attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, 2, 1, SCALE, jitter=1.0, jitter_seed=seed + 7)
         o1, _ = oracle.lse_merge(oc, lc, oo, lo)
         assert np.all(np.abs(o1 - o0) <= 1.01 * parts["allowance"] + 1e-12)
+
+
+@pytest.mark.parametrize("values", ["normal", "outliers"])
+def test_leaky_allowance_covers_score_error(values):
+    """R15 pin for the leaky variant (partial last P block, masked keys excluded from its scale):
+    jittering every score by up to its bound moves the output by at most the allowance, and the
+    jitter does flip codes."""
+    inp = _inputs(S=256, Hq=2, Hkv=1, seed=21, values=values)
+    z = oracle.quantize_all(inp.q, inp.k, inp.v)
+    o0, l0, al, le = oracle.attn_leaky(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 2, 1, SCALE, allowance=True)
+    plain, _ = oracle.attn_leaky(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 2, 1, SCALE)
+    assert np.array_equal(plain, o0)  # the allowance outputs do not change the result
+    flips = 0
+    for seed in range(3):
+        o1, l1 = oracle.attn_leaky(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, 2, 1, SCALE, jitter=1.0, jitter_seed=seed)
+        assert np.all(np.abs(o1 - o0) <= al + 1e-12)
+        assert np.all(np.abs(l1 - l0) <= 1.01 * le + 1e-12)
+        flips += int(np.sum(np.abs(o1 - o0) > 1e-3 * np.abs(o0) + 1e-9))
+    assert flips > 0
