@@ -4,14 +4,16 @@ One step is one pass of the whole forward path over one batch: MXFP8 quantisatio
 and V (columnwise + token-normalised), then the completed-block partial, the own-block partial and
 the LSE merge (bf16 output) -- by default in one fused kernel (`--path fused`), or as three separate
 kernels (`--path stepwise`) -- each call through the C ABI of libmxfa.so on torch's current stream.
+`--path leaky` times ordinary causal MXFP8 instead (the variant the method replaces), for the
+own-block/ordinary comparison the published timings make.
 Inputs are seeded synthetic bf16 tensors already resident in HBM when the timed region starts.
 
 Workload (the configuration the published forward timings are quoted on): B=1, 16 query heads,
 4 KV heads, S=32768, D=128, BSHD, causal, V rows scaled by 2^e, e ~ U{-4..4} per (token, kv-head).
 
 Prints one JSON line. `value` is TFLOP/s of the whole forward with the FlashAttention causal count
-2*B*Hq*S^2*D; `roofline` is the attention kernel (the dominant one: fused, or completed-block when
-stepwise) against the MXFP8 MFMA peak, from HIP events around its launches in the timed steps; `cpu_baseline` times the fp64 CPU
+2*B*Hq*S^2*D; `roofline` is the attention kernel (the dominant one: fused, leaky, or completed-block
+when stepwise) against the MXFP8 MFMA peak, from HIP events around its launches in the timed steps; `cpu_baseline` times the fp64 CPU
 oracle on a bounded row sample of the same workload.
 """
 from __future__ import annotations
@@ -91,7 +93,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa16x4_s32k_amplitudes")
-    ap.add_argument("--path", choices=["fused", "stepwise"], default="fused")
+    ap.add_argument("--path", choices=["fused", "stepwise", "leaky"], default="fused",
+                    help="fused (default): the leak-free forward in one attention kernel; stepwise: its three "
+                         "separate kernels; leaky: ordinary causal MXFP8 (the variant the method replaces)")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle CPU-baseline sample (0 skips)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the calibration for HBM counters")
@@ -135,7 +139,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     fused = args.path == "fused"
-    names = ["quantize_q", "quantize_k", "quantize_v"] + (["fused"] if fused else ["completed", "own_block", "merge"])
+    leaky = args.path == "leaky"
+    names = ["quantize_q", "quantize_k", "quantize_v"] + (
+        ["fused"] if fused else ["leaky"] if leaky else ["completed", "own_block", "merge"])
 
     def view(t):
         return mx.view_of(t, lay)
@@ -151,7 +157,11 @@ def main():
             lambda: L.mxfa_mxfp8_quantize(v.data_ptr(), B, S, Hkv, D, *vv[4:], mx.V, vc.data_ptr(), vcs.data_ptr(),
                                           vt.data_ptr(), vta.data_ptr(), sh),
         ]
-        if fused:
+        if leaky:
+            calls.append(lambda: L.mxfa_attn_fwd_leaky(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                                       vc.data_ptr(), vcs.data_ptr(), B, S, Hq, Hkv, D, w.scale,
+                                                       out.data_ptr(), *ov[4:], mx.OUT_BF16, lse.data_ptr(), sh))
+        elif fused:
             calls.append(lambda: L.mxfa_attn_fwd_fused(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
                                                        vc.data_ptr(), vcs.data_ptr(), vt.data_ptr(), vta.data_ptr(),
                                                        B, S, Hq, Hkv, D, w.scale, out.data_ptr(), *ov[4:],
@@ -194,8 +204,8 @@ def main():
     flops = 2.0 * B * Hq * S * S * D
     comp_flops = 512.0 * completed_pairs(B, Hq, S)
     own_flops = 512.0 * own_pairs(B, Hq, S)
-    attn_name = "fused" if fused else "completed"
-    attn_flops = comp_flops + own_flops if fused else comp_flops
+    attn_name = "fused" if fused else "leaky" if leaky else "completed"
+    attn_flops = comp_flops + own_flops if (fused or leaky) else comp_flops
     achieved = attn_flops / (per[attn_name] * 1e-3) / 1e12
     n_q, n_kv = B * Hq * S, B * Hkv * S
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
@@ -205,8 +215,8 @@ def main():
         "quantize_v": {"ms": per["quantize_v"],
                        "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32 + 1 + 1 / 128), per["quantize_v"])},
     }
-    if fused:
-        kernels["fused"] = {"ms": per["fused"], "TFLOP/s": achieved, "algorithmic_flop": attn_flops}
+    if fused or leaky:
+        kernels[attn_name] = {"ms": per[attn_name], "TFLOP/s": achieved, "algorithmic_flop": attn_flops}
     else:
         kernels["completed"] = {"ms": per["completed"], "TFLOP/s": achieved, "algorithmic_flop": comp_flops}
         kernels["own_block"] = {"ms": per["own_block"], "TFLOP/s": own_flops / (per["own_block"] * 1e-3) / 1e12,
@@ -238,7 +248,7 @@ def main():
                     for n, d in kernels.items()},
         "cpu_baseline": None,
     }
-    if args.cpu_rows > 0:
+    if args.cpu_rows > 0 and not leaky:  # the baseline times the oracle of the leak-free path
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
     print(json.dumps(res), flush=True)
 

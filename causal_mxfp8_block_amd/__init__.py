@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.mxfa_lse_merge.restype = I
         L.mxfa_attn_fwd_fused.argtypes = [P] * 8 + [I, I, I, I, I, F, P, I64, I64, I64, I, P, P]
         L.mxfa_attn_fwd_fused.restype = I
+        L.mxfa_attn_fwd_leaky.argtypes = six + [I, I, I, I, I, F, P, I64, I64, I64, I, P, P]
+        L.mxfa_attn_fwd_leaky.restype = I
         L.mxfa_attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
         L.mxfa_attn_fwd_workspace_bytes.restype = SZ
         L.mxfa_attn_fwd.argtypes = [P, I64, I64, I64] * 3 + [I, I, I, I, I, F, P, SZ, P, I64, I64, I64, I, P, P]
@@ -184,6 +186,23 @@ def attn_fwd_fused(qc, qs, kc, ks, vc, vcs, vt, vta, softmax_scale: float | None
     _, _, _, _, osb, oss, osh = view_of(out, layout)
     _check(lib().mxfa_attn_fwd_fused(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vcs), _p(vt), _p(vta), B, S, Hq, Hkv,
                                      D, scale, _p(out), osb, oss, osh, _out_code(out.dtype), _p(lse), _stream(qc)))
+    return out, lse
+
+
+def attn_fwd_leaky(qc, qs, kc, ks, vc, vcs, softmax_scale: float | None = None, out_dtype=torch.bfloat16,
+                   layout: str = "bshd", out=None, lse=None):
+    """Ordinary causal MXFP8 (leaks through V scales; for comparison): (out in ``layout``, lse [B,Hq,S])."""
+    B, Hq, S, D = qc.shape
+    Hkv = kc.shape[1]
+    scale = default_scale(D) if softmax_scale is None else softmax_scale
+    if out is None:
+        shape = (B, S, Hq, D) if layout == "bshd" else (S, B, Hq, D)
+        out = torch.empty(shape, dtype=out_dtype, device=qc.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=qc.device)
+    _, _, _, _, osb, oss, osh = view_of(out, layout)
+    _check(lib().mxfa_attn_fwd_leaky(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vcs), B, S, Hq, Hkv, D, scale, _p(out),
+                                     osb, oss, osh, _out_code(out.dtype), _p(lse), _stream(qc)))
     return out, lse
 
 

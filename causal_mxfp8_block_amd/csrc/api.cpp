@@ -253,6 +253,25 @@ MXFA_EXPORT int mxfa_attn_fwd_fused(const uint8_t* qc, const uint8_t* qs, const 
                     "attn_fwd_fused launch");
 }
 
+MXFA_EXPORT int mxfa_attn_fwd_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                                    const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D,
+                                    float softmax_scale, void* out, int64_t osb, int64_t oss, int64_t osh,
+                                    int out_dtype, float* lse_out, void* stream) {
+  g_last_error.clear();
+  TRY(check_attn_shape(B, S, Hq, Hkv, D));
+  const char* n[] = {"qc", "qs", "kc", "ks", "vc", "vcs"};
+  const void* p[] = {qc, qs, kc, ks, vc, vcs};
+  TRY(check_ptrs(n, p, 6));
+  if (out_dtype != MXFA_OUT_BF16 && out_dtype != MXFA_OUT_F32)
+    return fail(MXFA_ERR_UNSUPPORTED, "unknown output dtype %d", out_dtype);
+  TRY(check_view("out", out, B, S, Hq, osb, oss, osh, out_dtype == MXFA_OUT_BF16 ? 8 : 4));
+  if (lse_out && !aligned16(lse_out)) return fail(MXFA_ERR_ALIGN, "lse_out is not 16-byte aligned");
+  TRY(check_device());
+  return hip_status(mxfa::launch_attn_leaky(qc, qs, kc, ks, vc, vcs, B, S, Hq, Hkv, softmax_scale, out, osb, oss, osh,
+                                            out_dtype == MXFA_OUT_BF16, lse_out, static_cast<hipStream_t>(stream)),
+                    "attn_fwd_leaky launch");
+}
+
 MXFA_EXPORT size_t mxfa_attn_fwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D) {
   if (D != 128 || B < 1 || S < 1 || Hq < 1 || Hkv < 1) return 0;
   return carve(nullptr, B, S, Hq, Hkv).bytes;

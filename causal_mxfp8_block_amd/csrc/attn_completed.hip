@@ -185,12 +185,19 @@ __device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const
 }
 
 // Softmax, P quantisation and O^T += V^T P^T for one tile whose scores are in sacc. kFull: both
-// 32-key blocks are completed keys of this wave; otherwise only the first one is (the second one's
-// p is zero).
-template <bool kFull>
-__device__ __forceinline__ void softmax_pv(RowState& st, const v16f (&sacc)[2], const TileSmem& t, float scale_log2,
+// 32-key blocks are visible keys of this wave; otherwise only the first one is (the second one's p
+// is zero). kMaskBlk (ordinary causal variant only): that block is the wave's own 32-token block, of
+// which query qw + c sees keys qw .. qw + c; the others get p = 0, and its E8M0 comes from the
+// visible keys.
+template <bool kFull, int kMaskBlk = -1>
+__device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const TileSmem& t, float scale_log2,
                                            int c, int hf, bool first) {
   // Lane (c, hf), element i of block kt holds key 32kt + 16hf + i of the tile, query c.
+  if (kMaskBlk >= 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (16 * hf + i > c) sacc[kMaskBlk][i] = -INFINITY;
+  }
 
   // The V^T operands of this tile's P.V are read from LDS first, so their latency hides under the
   // softmax below. Lane (c, hf), tile dt: column 32dt + c, keys 16hf + [0,16) and 32 + 16hf + [0,16).
@@ -291,11 +298,16 @@ struct AttnParams {
 constexpr int CB_LDS_BYTES = 2 * sizeof(TileSmem);
 static_assert(4 * 32 * 128 * 2 <= CB_LDS_BYTES, "the own-block V must fit the tile buffers");
 
-// kFused = false: the completed-block partial (O_c, lse_c). kFused = true: the whole attention of
+// kMode: MODE_COMPLETED, the completed-block partial (O_c, lse_c); MODE_FUSED, the whole attention of
 // the row: completed blocks, the own block on the token-normalised V (TE#3865 Description, second
-// bullet), and the merge through the log-sum-exps, written once in the output's layout.
-template <bool kFused>
+// bullet), and the merge through the log-sum-exps, written once in the output's layout;
+// MODE_LEAKY, ordinary causal MXFP8 (keys j <= i, the own block through the same MXFP8 P.V with
+// its columnwise V scales, which also cover later tokens: the variant TE#3865 replaces, its
+// "MXFP8" column under Performance), written in the output's layout.
+enum : int { MODE_COMPLETED = 0, MODE_FUSED = 1, MODE_LEAKY = 2 };
+template <int kMode>
 __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
+  constexpr bool kFused = kMode == MODE_FUSED, kLeaky = kMode == MODE_LEAKY;
   __shared__ __align__(16) uint8_t lds[CB_LDS_BYTES];
   TileSmem* sm = reinterpret_cast<TileSmem*>(lds);  // sm[0], sm[1]
   const int S = P.S;
@@ -318,8 +330,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   const int qw = q0 + 32 * wave;          // first query of this wave; its completed keys are j < qw
   const bool wave_valid = qw < S;
   const int e_w = wave_valid ? qw : 0;
-  const int e_wg = min(q0 + 96, S - 32);  // key range end of the last valid wave
-  const int ntiles = (e_wg + CB_BN - 1) / CB_BN;
+  const int e_wg = min(q0 + 96, S - 32);  // completed-key range end of the last valid wave
+  // (the ordinary causal variant also reads the last wave's own block)
+  const int ntiles = (e_wg + (kLeaky ? 32 : 0) + CB_BN - 1) / CB_BN;
   const int64_t bhq = (int64_t)b * P.Hq + hq, bhk = (int64_t)b * P.Hkv + hk;
   // Buffer resources over this kv head's K codes [S,128], V codes [128,S] and K or V scales.
   const __amdgpu_buffer_rsrc_t rk =
@@ -380,8 +393,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
       scores<true>(sacc, cur, qop, qsc, c, hf);
       softmax_pv<true>(st, sacc, cur, scale_log2, c, hf, it == 0);
     } else if (kt0 < e_w) {
+      scores<kLeaky>(sacc, cur, qop, qsc, c, hf);
+      if (kLeaky)  // completed block, then the own block (masked)
+        softmax_pv<true, 1>(st, sacc, cur, scale_log2, c, hf, it == 0);
+      else
+        softmax_pv<false>(st, sacc, cur, scale_log2, c, hf, it == 0);
+    } else if (kLeaky && wave_valid && kt0 == e_w) {  // the own block opens this tile (masked)
       scores<false>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<false>(st, sacc, cur, scale_log2, c, hf, it == 0);
+      softmax_pv<false, 0>(st, sacc, cur, scale_log2, c, hf, it == 0);
     }
     if (it + 1 < ntiles) store_tile(sm[(it + 1) & 1], pk0, pk1, pv0, pv1, psc, tid);
     // Unconditional vmcnt(0): the prefetch is complete on every path out of the iteration (the
@@ -397,7 +416,31 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   const float lc_tot = la + lb;       // l of the completed partial (both lane halves)
   const bool empty = (e_w == 0);      // rows 0..31 have no completed key
 
-  if (!kFused) {
+  if (kLeaky) {
+    // O = acc / l and lse of the ordinary causal row (every row has at least its own key)
+    if (!wave_valid) return;
+    const float inv = 1.0f / lc_tot;
+    const int64_t off = b * P.osb + (int64_t)(qw + c) * P.oss + hq * P.osh + 4 * hf;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = st.o[dt][4 * g + e] * inv;
+        const int64_t o = off + 32 * dt + 8 * g;
+        if (P.out_bf16) {
+          uint2 pk;
+          pk.x = f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16);
+          pk.y = f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.out) + o) = pk;
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(P.out) + o) = make_float4(r[0], r[1], r[2], r[3]);
+        }
+      }
+    if (hf == 0 && P.lse_out) P.lse_out[bhq * S + qw + c] = (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
+    return;
+  } else if (!kFused) {
     if (!wave_valid) return;
     float* orow = P.o_c + (bhq * S + qw + c) * 128;
     const float inv = empty ? 0.f : 1.0f / lc_tot;
@@ -541,7 +584,7 @@ hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uin
   AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, B, S, Hq, Hkv, softmax_scale);
   p.o_c = o_c;
   p.lse_c = lse_c;
-  attn_kernel<false><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
+  attn_kernel<MODE_COMPLETED><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -558,7 +601,22 @@ hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t
   p.osh = osh;
   p.out_bf16 = out_bf16;
   p.lse_out = lse_out;
-  attn_kernel<true><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
+  attn_kernel<MODE_FUSED><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                             const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, float softmax_scale,
+                             void* out, int64_t osb, int64_t oss, int64_t osh, int out_bf16, float* lse_out,
+                             hipStream_t stream) {
+  AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, B, S, Hq, Hkv, softmax_scale);
+  p.out = out;
+  p.osb = osb;
+  p.oss = oss;
+  p.osh = osh;
+  p.out_bf16 = out_bf16;
+  p.lse_out = lse_out;
+  attn_kernel<MODE_LEAKY><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 

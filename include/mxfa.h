@@ -111,6 +111,19 @@ int mxfa_attn_fwd_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                         int Hq, int Hkv, int D, float softmax_scale, void* out, int64_t osb, int64_t oss,
                         int64_t osh, int out_dtype, float* lse_out, void* stream);
 
+/* attn_fwd_leaky -- ordinary causal MXFP8 attention, the variant the method replaces (TE #3865,
+ * Description, first paragraph, and the "MXFP8" column under Performance): for every (b, hq, i) all
+ * keys j <= i run through the completed-block computation of attn_fwd_completed_blocks, the query's
+ * own 32-key block included, with its columnwise V scale (which also covers the block's later
+ * tokens: the leak) and its P block's E8M0 taken from the visible keys. For comparison and leak
+ * demonstration only. Inputs as attn_fwd_completed_blocks; out is a [B,S,Hq,D] view (strides osb,
+ * oss, osh) written as bf16 (round to nearest even) or fp32 per out_dtype; lse_out fp32 [B,Hq,S]
+ * (natural log) may be NULL. */
+int mxfa_attn_fwd_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                        const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D,
+                        float softmax_scale, void* out, int64_t osb, int64_t oss, int64_t osh, int out_dtype,
+                        float* lse_out, void* stream);
+
 /* Bytes of workspace mxfa_attn_fwd needs (the MXFP8 codes and scales, 256-byte aligned parts). */
 size_t mxfa_attn_fwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D);
 

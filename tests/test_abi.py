@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["mxfa_mxfp8_quantize", "mxfa_attn_fwd_completed_blocks", "mxfa_attn_fwd_own_block",
-              "mxfa_lse_merge", "mxfa_attn_fwd", "mxfa_attn_fwd_fused", "mxfa_attn_fwd_workspace_bytes",
+              "mxfa_lse_merge", "mxfa_attn_fwd", "mxfa_attn_fwd_fused", "mxfa_attn_fwd_leaky",
+              "mxfa_attn_fwd_workspace_bytes",
               "mxfa_status_string",
               "mxfa_last_error"]:
         assert n in names
@@ -99,3 +100,21 @@ def test_no_device_is_an_error_not_a_crash():
     st, msg = _err(mx.lib().mxfa_attn_fwd_completed_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 128,
                                                            0.1, FAKE, FAKE, None))
     assert st == 5, msg
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(D=96), 3, "D = 96"),
+    (dict(S=40), 2, "multiple of 32"),
+    (dict(vc=None), 1, "vc is NULL"),
+    (dict(dtype=5), 3, "output dtype"),
+    (dict(osh=100), 4, "multiples of 8"),
+])
+def test_leaky_validation(args, status, needle):
+    a = dict(qc=FAKE, qs=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vcs=FAKE, B=1, S=64, Hq=4, Hkv=2, D=128, osh=128,
+             dtype=0)
+    a.update(args)
+    S, Hq = a["S"], a["Hq"]
+    st, msg = _err(mx.lib().mxfa_attn_fwd_leaky(a["qc"], a["qs"], a["kc"], a["ks"], a["vc"], a["vcs"], a["B"], S, Hq,
+                                                a["Hkv"], a["D"], 0.1, FAKE, S * Hq * 128, Hq * 128, a["osh"],
+                                                a["dtype"], None, None))
+    assert st == status and needle in msg, (st, msg)
