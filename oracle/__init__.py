@@ -50,6 +50,7 @@ def _load():
         lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.orc_e4m3_decode.restype = D
         lib.orc_quantize_rowwise.argtypes = [P, I, I, I, I, I64, I64, I64, P, P]
+        lib.orc_quantize_rows_f64.argtypes = [P, I64, I, P, P]
         lib.orc_quantize_v.argtypes = [P, I, I, I, I, I64, I64, I64, P, P, P, P]
         six = [P] * 6
         lib.orc_attn_completed.argtypes = six + [I, I, I, I, I, F, P, I, I, P, P, D, P, P, D, ctypes.c_uint64]
@@ -136,6 +137,18 @@ def quantize_rowwise(x) -> tuple[np.ndarray, np.ndarray]:
     codes = np.empty((v.B, v.H, v.S, v.D), np.uint8)
     scales = np.empty((v.B, v.H, v.S, v.D // 32), np.uint8)
     _load().orc_quantize_rowwise(_ptr(v.data), v.B, v.S, v.H, v.D, v.sb, v.ss, v.sh, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def quantize_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 of real-valued rows x [..., D] (blocks of 32 along D, rules O1/O2): (codes [..., D] u8,
+    scales [..., D/32] u8). Used for the block-scaled output."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    n = x.size // D
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1] + (D // 32,), np.uint8)
+    _load().orc_quantize_rows_f64(_ptr(x), n, D, _ptr(codes), _ptr(scales))
     return codes, scales
 
 

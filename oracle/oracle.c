@@ -146,6 +146,18 @@ void orc_quantize_rowwise(const uint16_t* x, int B, int S, int H, int D, int64_t
       }
 }
 
+/* MXFP8 of an output [cudnn-frontend PR #1088, PR summary: E4M3 O with one
+   UE8M0 scale per 32 elements of D]: the rows of x (fp64 values, n rows of D)
+   in blocks of 32 along D by O1 and O2, exactly as O4 does for bf16 rows. */
+void orc_quantize_rows_f64(const double* x, int64_t n, int D, uint8_t* codes, uint8_t* scales) {
+  assert(D % 32 == 0);
+  const int G = D / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int g = 0; g < G; ++g)
+      scales[r * G + g] = mx_block(x + r * D + 32 * g, 32, codes + r * D + 32 * g, 1);
+}
+
 /* O5 -- V columnwise: block u of column (b,h,d) is tokens [32u, 32u+32)
    [TE#3865 Description: "A columnwise MXFP8 V scale is shared by 32
    consecutive tokens"]. O6 -- the token-normalised copy: one amplitude per

@@ -43,6 +43,8 @@ uint8_t orc_e4m3_encode(double y);
 double orc_e4m3_decode(uint8_t code);
 
 /* O4: rowwise MXFP8 of a bf16 tensor [B,S,H,D] (by strides). */
+/* MXFP8 of fp64 rows (n rows of D): blocks of 32 along D by O1 and O2. */
+void orc_quantize_rows_f64(const double* x, int64_t n, int D, uint8_t* codes, uint8_t* scales);
 void orc_quantize_rowwise(const uint16_t* x, int B, int S, int H, int D, int64_t sb, int64_t ss, int64_t sh,
                           uint8_t* codes, uint8_t* scales);
 /* O5 + O6: V columnwise over 32 tokens, and the token-normalised copy. Any
