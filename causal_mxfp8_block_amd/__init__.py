@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.mxfa_lse_merge.restype = I
         L.mxfa_attn_fwd_fused.argtypes = [P] * 8 + [I, I, I, I, I, F, P, I64, I64, I64, I, P, P]
         L.mxfa_attn_fwd_fused.restype = I
+        L.mxfa_attn_fwd_fused_mxfp8.argtypes = [P] * 8 + [I, I, I, I, I, F, P, I64, I64, I64, P, P, P]
+        L.mxfa_attn_fwd_fused_mxfp8.restype = I
         L.mxfa_attn_fwd_leaky.argtypes = six + [I, I, I, I, I, F, P, I64, I64, I64, I, P, P]
         L.mxfa_attn_fwd_leaky.restype = I
         L.mxfa_attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -187,6 +189,23 @@ def attn_fwd_fused(qc, qs, kc, ks, vc, vcs, vt, vta, softmax_scale: float | None
     _check(lib().mxfa_attn_fwd_fused(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vcs), _p(vt), _p(vta), B, S, Hq, Hkv,
                                      D, scale, _p(out), osb, oss, osh, _out_code(out.dtype), _p(lse), _stream(qc)))
     return out, lse
+
+
+def attn_fwd_fused_mxfp8(qc, qs, kc, ks, vc, vcs, vt, vta, softmax_scale: float | None = None,
+                         layout: str = "bshd"):
+    """The fused forward with an MXFP8 output: (E4M3 codes u8 in ``layout`` [B,S,Hq,D] or [S,B,Hq,D],
+    E8M0 bytes u8 [B,Hq,S,D/32], lse [B,Hq,S])."""
+    B, Hq, S, D = qc.shape
+    Hkv = kc.shape[1]
+    scale = default_scale(D) if softmax_scale is None else softmax_scale
+    shape = (B, S, Hq, D) if layout == "bshd" else (S, B, Hq, D)
+    codes = torch.empty(shape, dtype=torch.uint8, device=qc.device)
+    sf_o = torch.empty((B, Hq, S, D // 32), dtype=torch.uint8, device=qc.device)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=qc.device)
+    _, _, _, _, osb, oss, osh = view_of(codes, layout)
+    _check(lib().mxfa_attn_fwd_fused_mxfp8(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vcs), _p(vt), _p(vta), B, S, Hq,
+                                           Hkv, D, scale, _p(codes), osb, oss, osh, _p(sf_o), _p(lse), _stream(qc)))
+    return codes, sf_o, lse
 
 
 def attn_fwd_leaky(qc, qs, kc, ks, vc, vcs, softmax_scale: float | None = None, out_dtype=torch.bfloat16,

@@ -253,6 +253,24 @@ MXFA_EXPORT int mxfa_attn_fwd_fused(const uint8_t* qc, const uint8_t* qs, const 
                     "attn_fwd_fused launch");
 }
 
+MXFA_EXPORT int mxfa_attn_fwd_fused_mxfp8(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
+                                          const uint8_t* ks, const uint8_t* vc, const uint8_t* vcs,
+                                          const uint8_t* vt, const uint8_t* vta, int B, int S, int Hq, int Hkv,
+                                          int D, float softmax_scale, uint8_t* o_codes, int64_t osb, int64_t oss,
+                                          int64_t osh, uint8_t* sf_o, float* lse_out, void* stream) {
+  g_last_error.clear();
+  TRY(check_attn_shape(B, S, Hq, Hkv, D));
+  const char* n[] = {"qc", "qs", "kc", "ks", "vc", "vcs", "vt", "vta", "sf_o"};
+  const void* p[] = {qc, qs, kc, ks, vc, vcs, vt, vta, sf_o};
+  TRY(check_ptrs(n, p, 9));
+  TRY(check_view("o_codes", o_codes, B, S, Hq, osb, oss, osh, 16));
+  if (lse_out && !aligned16(lse_out)) return fail(MXFA_ERR_ALIGN, "lse_out is not 16-byte aligned");
+  TRY(check_device());
+  return hip_status(mxfa::launch_attn_fused(qc, qs, kc, ks, vc, vcs, vt, vta, B, S, Hq, Hkv, softmax_scale, o_codes,
+                                            osb, oss, osh, 0, lse_out, static_cast<hipStream_t>(stream), sf_o),
+                    "attn_fwd_fused_mxfp8 launch");
+}
+
 MXFA_EXPORT int mxfa_attn_fwd_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                     const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, int D,
                                     float softmax_scale, void* out, int64_t osb, int64_t oss, int64_t osh,

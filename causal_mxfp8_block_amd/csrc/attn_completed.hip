@@ -289,6 +289,8 @@ struct AttnParams {
   void* out;                                     // final output view (fused)
   int64_t osb, oss, osh;
   int out_bf16;
+  int out_mxfp8;                                 // fused: O as E4M3 codes + one E8M0 per 32 columns
+  uint8_t* sf_o;                                 // ... those E8M0 bytes, [B,Hq,S,D/32]
   float* lse_out;                                // may be null (fused)
 };
 
@@ -545,11 +547,35 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
         const float a = u2f((uint32_t)vown[j * 128 + 32 * dt + c] << 16);
         oo = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pa[u], oo, 0, 0, 0);
       }
+      float rr[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rr[e] = st.o[dt][e] * fc + oo[e] * fo;
+      if (P.out_mxfp8) {
+        // Block-scaled O (MXFP8, as the block-scaled O epilogue of cudnn-frontend PR #1088): one E8M0
+        // per 32 columns 32dt .. 32dt+31 -- this lane holds 16 of them, lane ^ 32 the rest -- by the
+        // same rule as the input quantiser (smallest k with amax <= 448 * 2^k), then the E4M3 codes of
+        // x * 2^-k (exact scaling, round to nearest even).
+        float am = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) am = vmax(am, fabsf(rr[e]));
+        float am2 = am;
+        swap32f(am, am2);
+        am = vmax(am, am2);
+        const int k = e8m0_exponent(am);
+        const float m = pow2_neg(k);
+        uint8_t* ob = reinterpret_cast<uint8_t*>(P.out);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint32_t*>(ob + off + 32 * dt + 8 * g) =
+              pack4_e4m3(rr[4 * g] * m, rr[4 * g + 1] * m, rr[4 * g + 2] * m, rr[4 * g + 3] * m);
+        if (hf == 0) P.sf_o[(bhq * S + q) * 4 + dt] = (uint8_t)(k + 127);
+        continue;
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float r[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = st.o[dt][4 * g + e] * fc + oo[4 * g + e] * fo;
+        for (int e = 0; e < 4; ++e) r[e] = rr[4 * g + e];
         const int64_t o = off + 32 * dt + 8 * g;
         if (P.out_bf16) {
           uint2 pk;
@@ -591,7 +617,7 @@ hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uin
 hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                              const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B,
                              int S, int Hq, int Hkv, float softmax_scale, void* out, int64_t osb, int64_t oss,
-                             int64_t osh, int out_bf16, float* lse_out, hipStream_t stream) {
+                             int64_t osh, int out_bf16, float* lse_out, hipStream_t stream, uint8_t* sf_o) {
   AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, B, S, Hq, Hkv, softmax_scale);
   p.vt = vt;
   p.vta = vta;
@@ -600,6 +626,8 @@ hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t
   p.oss = oss;
   p.osh = osh;
   p.out_bf16 = out_bf16;
+  p.out_mxfp8 = sf_o != nullptr;
+  p.sf_o = sf_o;
   p.lse_out = lse_out;
   attn_kernel<MODE_FUSED><<<dim3((unsigned)(p.n_qtiles * p.n_pairs)), dim3(256), 0, stream>>>(p);
   return hipGetLastError();

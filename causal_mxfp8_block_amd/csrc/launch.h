@@ -16,7 +16,8 @@ hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uin
 hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                              const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B,
                              int S, int Hq, int Hkv, float softmax_scale, void* out, int64_t osb, int64_t oss,
-                             int64_t osh, int out_bf16, float* lse_out, hipStream_t stream);
+                             int64_t osh, int out_bf16, float* lse_out, hipStream_t stream,
+                             uint8_t* sf_o = nullptr);  // sf_o != null: MXFP8 O codes into out
 hipError_t launch_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                              const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, float softmax_scale,
                              void* out, int64_t osb, int64_t oss, int64_t osh, int out_bf16, float* lse_out,

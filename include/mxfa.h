@@ -111,6 +111,19 @@ int mxfa_attn_fwd_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                         int Hq, int Hkv, int D, float softmax_scale, void* out, int64_t osb, int64_t oss,
                         int64_t osh, int out_dtype, float* lse_out, void* stream);
 
+/* attn_fwd_fused_mxfp8 -- attn_fwd_fused with the output itself in MXFP8, for a downstream MXFP8
+ * GEMM (the block-scaled O epilogue of cudnn-frontend PR #1088, PR summary: E4M3 O with one UE8M0
+ * scale per 32 elements of D, the scales in a separate output). Each row's fp32 output, before any
+ * rounding to bf16, is quantised per 32 columns by the rule of mxfa_mxfp8_quantize (smallest k with
+ * amax <= 448 * 2^k; codes of x * 2^-k, round to nearest even). o_codes: u8 E4M3 codes through the
+ * [B,S,Hq,D] view (element strides osb, oss, osh, multiples of 16; 16-byte aligned); sf_o: u8 E8M0
+ * bytes [B,Hq,S,D/32], row-major (this library's own layout, 2^(byte-127)); lse_out fp32 [B,Hq,S]
+ * may be NULL. */
+int mxfa_attn_fwd_fused_mxfp8(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                              const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B,
+                              int S, int Hq, int Hkv, int D, float softmax_scale, uint8_t* o_codes, int64_t osb,
+                              int64_t oss, int64_t osh, uint8_t* sf_o, float* lse_out, void* stream);
+
 /* attn_fwd_leaky -- ordinary causal MXFP8 attention, the variant the method replaces (TE #3865,
  * Description, first paragraph, and the "MXFP8" column under Performance): for every (b, hq, i) all
  * keys j <= i run through the completed-block computation of attn_fwd_completed_blocks, the query's
