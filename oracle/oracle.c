@@ -565,3 +565,103 @@ void orc_attn_identity(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh,
   free(K);
   free(V);
 }
+
+/* ------------------------------------------------------------- backward --- */
+
+/* Backward on decoded operands [TE#3865 Description, backward bullet: BF16
+   backward on Q/K decoded from their rowwise MXFP8 bytes and V decoded from
+   the token-normalised copy]: the gradients of causal softmax attention
+   O = softmax(scale Q K^T) V at the real-valued operands Q, K, V, with the
+   forward's O and lse (natural log) as the softmax statistics and dO the
+   output gradient:
+     Delta_i = sum_d dO_i,d O_i,d
+     P_ij    = exp(scale Q_i . K_j - lse_i)                    (j <= i)
+     dS_ij   = P_ij (dO_i . V_j - Delta_i)
+     dQ_i    = scale sum_{j <= i} dS_ij K_j
+     dK_j    = scale sum_{hq of kv head} sum_{i >= j} dS_ij Q_i
+     dV_j    = sum_{hq of kv head} sum_{i >= j} P_ij dO_i
+   Q, O, dO [B,Hq,S,D], K, V [B,Hkv,S,D], lse [B,Hq,S]. dq for the query rows
+   qrows (nq of them; NULL: all S) into [B,Hq,nq,D]; dk and dv for the key rows
+   krows (nk; NULL: all) into [B,Hkv,nk,D]. Any output may be NULL. */
+void orc_attn_bwd_values(const double* Q, const double* K, const double* V, const double* O, const double* dO,
+                         const double* lse, int B, int S, int Hq, int Hkv, int D, double scale,
+                         const int32_t* qrows, int nq, const int32_t* krows, int nk, double* dq, double* dk,
+                         double* dv) {
+  const int G = Hq / Hkv;
+  double* delta = (double*)malloc(sizeof(double) * (int64_t)B * Hq * S);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < (int64_t)B * Hq * S; ++r) delta[r] = dot(dO + r * D, O + r * D, D);
+  if (dq) {
+#pragma omp parallel for collapse(3) schedule(dynamic, 4)
+    for (int b = 0; b < B; ++b)
+      for (int hq = 0; hq < Hq; ++hq)
+        for (int r = 0; r < nq; ++r) {
+          const int i = row_index(qrows, r), hk = hq / G;
+          const int64_t qi = (((int64_t)b * Hq + hq) * S + i);
+          const double* Kh = K + ((int64_t)b * Hkv + hk) * S * D;
+          const double* Vh = V + ((int64_t)b * Hkv + hk) * S * D;
+          double* out = dq + (((int64_t)b * Hq + hq) * nq + r) * D;
+          for (int d = 0; d < D; ++d) out[d] = 0.0;
+          for (int j = 0; j <= i; ++j) {
+            const double p = exp(scale * dot(Q + qi * D, Kh + (int64_t)j * D, D) - lse[qi]);
+            const double ds = p * (dot(dO + qi * D, Vh + (int64_t)j * D, D) - delta[qi]);
+            for (int d = 0; d < D; ++d) out[d] += ds * Kh[(int64_t)j * D + d];
+          }
+          for (int d = 0; d < D; ++d) out[d] *= scale;
+        }
+  }
+  if (dk || dv) {
+#pragma omp parallel for collapse(3) schedule(dynamic, 4)
+    for (int b = 0; b < B; ++b)
+      for (int hk = 0; hk < Hkv; ++hk)
+        for (int r = 0; r < nk; ++r) {
+          const int j = row_index(krows, r);
+          const double* kj = K + (((int64_t)b * Hkv + hk) * S + j) * D;
+          const double* vj = V + (((int64_t)b * Hkv + hk) * S + j) * D;
+          double* ak = (double*)calloc(D, sizeof(double));
+          double* av = (double*)calloc(D, sizeof(double));
+          for (int hq = hk * G; hq < (hk + 1) * G; ++hq)
+            for (int i = j; i < S; ++i) {
+              const int64_t qi = (((int64_t)b * Hq + hq) * S + i);
+              const double p = exp(scale * dot(Q + qi * D, kj, D) - lse[qi]);
+              const double ds = p * (dot(dO + qi * D, vj, D) - delta[qi]);
+              for (int d = 0; d < D; ++d) {
+                av[d] += p * dO[qi * D + d];
+                ak[d] += ds * Q[qi * D + d];
+              }
+            }
+          const int64_t orow = (((int64_t)b * Hkv + hk) * nk + r) * D;
+          for (int d = 0; d < D; ++d) {
+            if (dk) dk[orow + d] = scale * ak[d];
+            if (dv) dv[orow + d] = av[d];
+          }
+          free(ak);
+          free(av);
+        }
+  }
+  free(delta);
+}
+
+/* The same from the codes in the library's layouts: Q, K decoded from their
+   rowwise MXFP8 bytes (O4/O3), V from the token-normalised copy (O6/O3); O and
+   dO bf16 [B,S,Hq,D] views, lse fp32 [B,Hq,S]. */
+void orc_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
+                  const uint8_t* vta, const uint16_t* o, int64_t osb, int64_t oss, int64_t osh, const float* lse,
+                  const uint16_t* dout, int64_t gsb, int64_t gss, int64_t gsh, int B, int S, int Hq, int Hkv, int D,
+                  float scale, const int32_t* qrows, int nq, const int32_t* krows, int nk, double* dq, double* dk,
+                  double* dv) {
+  double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
+  double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
+  double* V = decode_vtn(vt, vta, B, Hkv, S, D);
+  double* Ov = bf16_tensor(o, osb, oss, osh, B, S, Hq, D);
+  double* dOv = bf16_tensor(dout, gsb, gss, gsh, B, S, Hq, D);
+  double* L = (double*)malloc(sizeof(double) * (int64_t)B * Hq * S);
+  for (int64_t r = 0; r < (int64_t)B * Hq * S; ++r) L[r] = (double)lse[r];
+  orc_attn_bwd_values(Q, K, V, Ov, dOv, L, B, S, Hq, Hkv, D, (double)scale, qrows, nq, krows, nk, dq, dk, dv);
+  free(Q);
+  free(K);
+  free(V);
+  free(Ov);
+  free(dOv);
+  free(L);
+}
