@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.mxfa_attn_fwd_fused.restype = I
         L.mxfa_attn_fwd_fused_mxfp8.argtypes = [P] * 8 + [I, I, I, I, I, F, P, I64, I64, I64, P, P, P]
         L.mxfa_attn_fwd_fused_mxfp8.restype = I
+        L.mxfa_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.mxfa_attn_bwd_workspace_bytes.restype = SZ
+        L.mxfa_attn_bwd.argtypes = six + [P, P, P, I, I, I, I, I, F, I64, I64, I64, I64, I64, I64, P, SZ, P, P, P, P]
+        L.mxfa_attn_bwd.restype = I
         L.mxfa_attn_fwd_leaky.argtypes = six + [I, I, I, I, I, F, P, I64, I64, I64, I, P, P]
         L.mxfa_attn_fwd_leaky.restype = I
         L.mxfa_attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -250,3 +254,29 @@ def attn_fwd(q, k, v, softmax_scale: float | None = None, layout: str = "bshd", 
                                scale, _p(workspace), workspace.numel(), _p(out), osb, oss, osh,
                                _out_code(out.dtype), _p(lse), _stream(q)))
     return out, lse
+
+
+def attn_bwd(qc, qs, kc, ks, vt, vta, o, lse, do, softmax_scale: float | None = None, layout: str = "bshd",
+             workspace=None):
+    """Backward on decoded operands: (dq like ``o``, dk, dv [B,S,Hkv,D] (or [S,B,Hkv,D]) bf16).
+
+    o and do are the forward's output and its gradient, bf16 in ``layout``; lse the forward's [B,Hq,S]."""
+    B, Hq, S, D = qc.shape
+    Hkv = kc.shape[1]
+    scale = default_scale(D) if softmax_scale is None else softmax_scale
+    if do.stride() != o.stride():
+        do = do.contiguous() if o.is_contiguous() else torch.empty_like(o).copy_(do)
+    dq = torch.empty_like(o)
+    kshape = (B, S, Hkv, D) if layout == "bshd" else (S, B, Hkv, D)
+    dk = torch.empty(kshape, dtype=torch.bfloat16, device=qc.device)
+    dv = torch.empty(kshape, dtype=torch.bfloat16, device=qc.device)
+    need = int(lib().mxfa_attn_bwd_workspace_bytes(B, S, Hq, Hkv, D))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qc.device)
+    _, _, _, _, qsb, qss, qsh = view_of(o, layout)
+    _, _, _, _, ksb, kss, ksh = view_of(dk, layout)
+    _check(lib().mxfa_attn_bwd(_p(qc), _p(qs), _p(kc), _p(ks), _p(vt), _p(vta), _p(o), _p(lse), _p(do), B, S, Hq,
+                               Hkv, D, scale, qsb, qss, qsh, ksb, kss, ksh, _p(workspace), workspace.numel(), _p(dq),
+                               _p(dk), _p(dv), _stream(qc)))
+    return dq, dk, dv
+

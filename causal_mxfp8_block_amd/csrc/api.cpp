@@ -127,6 +127,27 @@ Workspace carve(void* base, int B, int S, int Hq, int Hkv) {
   return w;
 }
 
+mxfa::BwdWorkspace carve_bwd(void* base, int B, int S, int Hq, int Hkv) {
+  mxfa::BwdWorkspace w{};
+  const size_t nq = (size_t)B * Hq * S * 128 * 2, nk = (size_t)B * Hkv * S * 128 * 2;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    uint8_t* p = base ? static_cast<uint8_t*>(base) + off : nullptr;
+    off += align256(n);
+    return p;
+  };
+  w.qd = reinterpret_cast<uint16_t*>(take(nq));
+  w.qdt = reinterpret_cast<uint16_t*>(take(nq));
+  w.kd = reinterpret_cast<uint16_t*>(take(nk));
+  w.kdt = reinterpret_cast<uint16_t*>(take(nk));
+  w.vd = reinterpret_cast<uint16_t*>(take(nk));
+  w.gd = reinterpret_cast<uint16_t*>(take(nq));
+  w.gdt = reinterpret_cast<uint16_t*>(take(nq));
+  w.delta = reinterpret_cast<float*>(take((size_t)B * Hq * S * 4));
+  w.bytes = off;
+  return w;
+}
+
 }  // namespace
 
 MXFA_EXPORT const char* mxfa_status_string(int status) {
@@ -326,3 +347,39 @@ MXFA_EXPORT int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t q
                                            st),
                     "fused attention");
 }
+
+MXFA_EXPORT size_t mxfa_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D) {
+  if (D != 128 || B < 1 || S < 1 || Hq < 1 || Hkv < 1) return 0;
+  return carve_bwd(nullptr, B, S, Hq, Hkv).bytes;
+}
+
+MXFA_EXPORT int mxfa_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                              const uint8_t* vt, const uint8_t* vta, const void* o, const float* lse, const void* dout,
+                              int B, int S, int Hq, int Hkv, int D, float softmax_scale, int64_t qsb, int64_t qss,
+                              int64_t qsh, int64_t ksb, int64_t kss, int64_t ksh, void* workspace,
+                              size_t workspace_bytes, void* dq, void* dk, void* dv, void* stream) {
+  g_last_error.clear();
+  TRY(check_attn_shape(B, S, Hq, Hkv, D));
+  const char* n[] = {"qc", "qs", "kc", "ks", "vt", "vta", "lse"};
+  const void* p[] = {qc, qs, kc, ks, vt, vta, lse};
+  TRY(check_ptrs(n, p, 7));
+  TRY(check_view("o", o, B, S, Hq, qsb, qss, qsh, 8));
+  TRY(check_view("dout", dout, B, S, Hq, qsb, qss, qsh, 8));
+  TRY(check_view("dq", dq, B, S, Hq, qsb, qss, qsh, 8));
+  TRY(check_view("dk", dk, B, S, Hkv, ksb, kss, ksh, 8));
+  TRY(check_view("dv", dv, B, S, Hkv, ksb, kss, ksh, 8));
+  if (!workspace) return fail(MXFA_ERR_NULL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(MXFA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  const mxfa::BwdWorkspace w = carve_bwd(workspace, B, S, Hq, Hkv);
+  if (workspace_bytes < w.bytes)
+    return fail(MXFA_ERR_UNSUPPORTED, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                w.bytes);
+  TRY(check_device());
+  return hip_status(mxfa::launch_attn_bwd(qc, qs, kc, ks, vt, vta, static_cast<const uint16_t*>(o), lse,
+                                          static_cast<const uint16_t*>(dout), B, S, Hq, Hkv, softmax_scale, qsb, qss,
+                                          qsh, ksb, kss, ksh, w, static_cast<uint16_t*>(dq),
+                                          static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv),
+                                          static_cast<hipStream_t>(stream)),
+                    "attn_bwd launch");
+}
+

@@ -1,0 +1,374 @@
+// attn_bwd.hip -- backward of leak-free causal MXFP8 attention on decoded operands, gfx950.
+//
+// TransformerEngine PR #3865, "Description", backward bullet: the backward runs in BF16 on Q/K decoded
+// from their rowwise MXFP8 bytes and V decoded from the token-normalised copy, so no gradient depends
+// on a later token through a shared scale. With the forward's O and LSE as the softmax statistics:
+//   Delta_i = dO_i . O_i,   P_ij = exp(scale Q_i.K_j - lse_i) (j <= i),   dS_ij = P_ij (dO_i.V_j - Delta_i)
+//   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i,   dV_j = sum_i P_ij dO_i
+// (dK, dV summed over the query heads of a KV head).
+//
+// Design (CDNA4, wave64, bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//  * A preparation pass decodes Q, K and V to bf16 (exact: an E4M3 value times a power of two has 4
+//    significant bits) and copies dO, each head-major, plus a transposed [D][S] copy of Q, K and dO
+//    for the MFMA operands that contract over tokens; it also forms Delta.
+//  * dK/dV kernel: one wave per 32 keys, their K and V operands held in registers. For every query
+//    head of the KV head and every 32-query block at or after the keys, it computes S = Q K^T and
+//    dP = dO V^T (keys on the lanes, queries on the accumulator elements), P and dS elementwise, and
+//    accumulates dV^T += dO^T P and dK^T += Q^T dS. P and dS stay in their accumulator registers and
+//    are the B operand of those MFMAs: the accumulator's query order is a permutation of the B
+//    operand's contraction order, and the A operand (dO^T, Q^T, read from LDS) is read in the same
+//    permuted order.
+//  * dQ kernel: one wave per 32 queries, their Q and dO operands in registers. For every 32-key block
+//    at or before the queries it computes S^T = K Q^T and dP^T = V dO^T (queries on the lanes: lse and
+//    Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way.
+//  * The 32-token blocks on the diagonal mask key > query; blocks beyond it are skipped.
+//  * Query (dK/dV) and key (dQ) blocks are staged in LDS per workgroup of 4 waves, rows padded so
+//    that the 16- and 8-byte operand reads are bank-conflict-free.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxfa {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int BW_ROW = 136;  // LDS pitch (bf16) of a [token][D] tile row: 128 + 8 pad
+constexpr int BW_TROW = 36;  // LDS pitch (bf16) of a [D][32 tokens] tile row: 32 + 4 pad
+
+__device__ __forceinline__ v8bf ld8bf(const uint16_t* p) {  // 16 bytes, 16-byte aligned
+  return __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(p));
+}
+// Two 8-byte halves (4 bf16 each) into one operand.
+__device__ __forceinline__ v8bf ld4x2bf(const uint16_t* p0, const uint16_t* p1) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p0), b = *reinterpret_cast<const uint2*>(p1);
+  return __builtin_bit_cast(v8bf, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Elements 8t .. 8t+7 of an accumulator as bf16 (round to nearest even).
+__device__ __forceinline__ v8bf to_bf16(const v16f& x, int t) {
+  v8bf r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[8 * t + e];
+  return r;
+}
+
+// ---- preparation -------------------------------------------------------------------------------
+// One workgroup per (b, h, 64-token tile), 256 threads: thread g handles token g/4, columns
+// 32(g%4) .. +32. Source kSrc: 0 rowwise codes + E8M0 per 32 columns, 1 token-normalised codes + one
+// E8M0 amplitude per token, 2 a bf16 [B,S,H,D] view (with Delta from the o view when delta != null).
+// Writes the bf16 rows to out [B,H,S,D] and, when out_t != null, the transposed out_t [B,H,D,S].
+template <int kSrc>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, const uint8_t* scales, const uint16_t* x,
+                                                       int64_t sb, int64_t ss, int64_t sh, const uint16_t* o,
+                                                       int64_t osb, int64_t oss, int64_t osh, int S, int H,
+                                                       uint16_t* out, uint16_t* out_t, float* delta) {
+  __shared__ __align__(16) uint16_t tile[64 * BW_ROW];
+  const int g = threadIdx.x, tok = g >> 2, c0 = (g & 3) * 32;
+  const int s0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int s = s0 + tok;
+  const int64_t bh = (int64_t)b * H + h;
+  uint32_t w[16];  // 32 bf16, packed in pairs
+  if (s < S) {
+    if (kSrc == 2) {
+      const uint16_t* row = x + b * sb + (int64_t)s * ss + h * sh + c0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = reinterpret_cast<const uint4*>(row)[q];
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+      if (delta) {
+        const uint16_t* orow = o + b * osb + (int64_t)s * oss + h * osh + c0;
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = reinterpret_cast<const uint4*>(orow)[q];
+          const uint32_t ov[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t gw = w[4 * q + e];
+            acc = fmaf(bf16_to_f32(gw & 0xffffu), bf16_to_f32(ov[e] & 0xffffu), acc);
+            acc = fmaf(bf16_to_f32(gw >> 16), bf16_to_f32(ov[e] >> 16), acc);
+          }
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        if ((g & 3) == 0) delta[bh * S + s] = acc;
+      }
+    } else {
+      const uint8_t* crow = codes + (bh * S + s) * 128 + c0;
+      const float sc = kSrc == 0 ? e8m0_to_f32(scales[(bh * S + s) * 4 + (g & 3)]) : e8m0_to_f32(scales[bh * S + s]);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 v = reinterpret_cast<const uint4*>(crow)[q];
+        const uint32_t cw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // E4M3 value times a power of two has at most 4 significant bits: its top 16 bits are the bf16
+          const uint32_t lo0 = f2u(e4m3_to_f32(cw[e] & 0xffu) * sc) >> 16;
+          const uint32_t hi0 = f2u(e4m3_to_f32((cw[e] >> 8) & 0xffu) * sc) >> 16;
+          const uint32_t lo1 = f2u(e4m3_to_f32((cw[e] >> 16) & 0xffu) * sc) >> 16;
+          const uint32_t hi1 = f2u(e4m3_to_f32(cw[e] >> 24) * sc) >> 16;
+          w[8 * q + 2 * e] = lo0 | (hi0 << 16);
+          w[8 * q + 2 * e + 1] = lo1 | (hi1 << 16);
+        }
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out + (bh * S + s) * 128 + c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  }
+  if (!out_t) return;
+  uint4* trow = reinterpret_cast<uint4*>(tile + tok * BW_ROW + c0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) trow[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  __syncthreads();
+  // transposed: thread g writes column d = g/2, tokens 32(g%2) .. +32 of this tile
+  const int d = g >> 1, t0 = (g & 1) * 32;
+  if (s0 + t0 >= S) return;  // S % 32 == 0: a half tile is either wholly inside or wholly outside
+  uint32_t p[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    p[e] = (uint32_t)tile[(t0 + 2 * e) * BW_ROW + d] | ((uint32_t)tile[(t0 + 2 * e + 1) * BW_ROW + d] << 16);
+  uint4* tdst = reinterpret_cast<uint4*>(out_t + (bh * 128 + d) * S + s0 + t0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) tdst[q] = make_uint4(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+}
+
+struct BwdParams {
+  const uint16_t *qd, *qdt, *kd, *kdt, *vd, *gd, *gdt;  // decoded operands (workspace)
+  const float *lse, *delta;                              // [B,Hq,S]
+  int S, Hq, Hkv;
+  float scale, scale_log2;
+  uint16_t *dq, *dk, *dv;                                // bf16 outputs (views)
+  int64_t qsb, qss, qsh, ksb, kss, ksh;                 // strides of dq and of dk/dv
+};
+
+// Stage a 32-token x 128 row-major block (src rows t0..t0+31 of a [S][128] bf16 head) into LDS.
+__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int t0, int tid) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + 256 * r, row = idx >> 4, col = (idx & 15) * 8;
+    *reinterpret_cast<uint4*>(dst + row * BW_ROW + col) =
+        *reinterpret_cast<const uint4*>(src + (int64_t)(t0 + row) * 128 + col);
+  }
+}
+// Stage the 128 x 32-token block (columns t0..t0+31 of a [128][S] transposed head) into LDS.
+__device__ __forceinline__ void stage_cols(uint16_t* dst, const uint16_t* src, int S, int t0, int tid) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + 256 * r, d = idx >> 2, col = (idx & 3) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)d * S + t0 + col);
+    uint2* p = reinterpret_cast<uint2*>(dst + d * BW_TROW + col);  // rows are 8-byte aligned
+    p[0] = make_uint2(v.x, v.y);
+    p[1] = make_uint2(v.z, v.w);
+  }
+}
+
+// ---- dK, dV ------------------------------------------------------------------------------------
+// Workgroup: 4 waves = keys 128 kt .. 128 kt + 127 of (b, hk); wave w owns keys 32(4kt + w) + [0, 32).
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams P) {
+  __shared__ __align__(16) uint16_t sQ[32 * BW_ROW], sG[32 * BW_ROW], sQt[128 * BW_TROW], sGt[128 * BW_TROW];
+  __shared__ __align__(16) float sL[32], sD[32];
+  const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int G = P.Hq / P.Hkv;
+  const int kb = 4 * kt + wave, key0 = 32 * kb;
+  const bool valid = key0 < S;
+  const int64_t bhk = (int64_t)b * P.Hkv + hk;
+  // This wave's K and V rows as B operands: lane (key c, h), step s holds columns 16s + 8h + [0, 8).
+  v8bf kop[8], vop[8];
+  const int krow = valid ? key0 + c : 0;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    kop[s] = ld8bf(P.kd + (bhk * S + krow) * 128 + 16 * s + 8 * h);
+    vop[s] = ld8bf(P.vd + (bhk * S + krow) * 128 + 16 * s + 8 * h);
+  }
+  v16f dkT[4], dvT[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
+  const int nqb = S / 32;
+  for (int hq = hk * G; hq < (hk + 1) * G; ++hq) {
+    const int64_t bhq = (int64_t)b * P.Hq + hq;
+    const uint16_t *qd = P.qd + bhq * S * 128, *gd = P.gd + bhq * S * 128;
+    const uint16_t *qdt = P.qdt + bhq * 128 * S, *gdt = P.gdt + bhq * 128 * S;
+    for (int qb = 4 * kt; qb < nqb; ++qb) {
+      const int q0 = 32 * qb;
+      stage_rows(sQ, qd, q0, tid);
+      stage_rows(sG, gd, q0, tid);
+      stage_cols(sQt, qdt, S, q0, tid);
+      stage_cols(sGt, gdt, S, q0, tid);
+      if (tid < 32) {
+        sL[tid] = P.lse[bhq * S + q0 + tid] * 1.4426950408889634f;
+        sD[tid] = P.delta[bhq * S + q0 + tid];
+      }
+      __syncthreads();
+      if (valid && qb >= kb) {
+        // S = Q K^T and dP = dO V^T: lane (key c, h), element i <-> query 8(i/4) + 4h + i%4 of the block
+        v16f sacc, pacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          sacc = mfma_bf16(ld8bf(sQ + c * BW_ROW + 16 * s + 8 * h), kop[s], sacc);
+          pacc = mfma_bf16(ld8bf(sG + c * BW_ROW + 16 * s + 8 * h), vop[s], pacc);
+        }
+        const bool diag = qb == kb;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(sL + 8 * g4 + 4 * h);
+          const float4 d4 = *reinterpret_cast<const float4*>(sD + 8 * g4 + 4 * h);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g4 + e, qq = 8 * g4 + 4 * h + e;
+            float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lv[e]));
+            if (diag && c > qq) p = 0.f;
+            sacc[i] = p;                       // P
+            pacc[i] = p * (pacc[i] - dv[e]);   // dS
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries, two 16-query steps. Step t, B slot
+        // (h, e) is accumulator element 8t + e: query 16t + 8(e/4) + 4h + e%4; the A operand (row d)
+        // reads those queries from the transposed tile.
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const v8bf pb = to_bf16(sacc, t), sb = to_bf16(pacc, t);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int d = 32 * dt + c;
+            const v8bf ga = ld4x2bf(sGt + d * BW_TROW + 16 * t + 4 * h, sGt + d * BW_TROW + 16 * t + 8 + 4 * h);
+            const v8bf qa = ld4x2bf(sQt + d * BW_TROW + 16 * t + 4 * h, sQt + d * BW_TROW + 16 * t + 8 + 4 * h);
+            dvT[dt] = mfma_bf16(ga, pb, dvT[dt]);
+            dkT[dt] = mfma_bf16(qa, sb, dkT[dt]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!valid) return;
+  // lane (key c, h), element i of tile dt: column 32dt + 8(i/4) + 4h + i%4
+  const int64_t off = b * P.ksb + (int64_t)(key0 + c) * P.kss + hk * P.ksh + 4 * h;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int64_t o = off + 32 * dt + 8 * g4;
+      uint2 pk, pv;
+      pk.x = f32_to_bf16(dkT[dt][4 * g4] * P.scale) | (f32_to_bf16(dkT[dt][4 * g4 + 1] * P.scale) << 16);
+      pk.y = f32_to_bf16(dkT[dt][4 * g4 + 2] * P.scale) | (f32_to_bf16(dkT[dt][4 * g4 + 3] * P.scale) << 16);
+      pv.x = f32_to_bf16(dvT[dt][4 * g4]) | (f32_to_bf16(dvT[dt][4 * g4 + 1]) << 16);
+      pv.y = f32_to_bf16(dvT[dt][4 * g4 + 2]) | (f32_to_bf16(dvT[dt][4 * g4 + 3]) << 16);
+      *reinterpret_cast<uint2*>(P.dk + o) = pk;
+      *reinterpret_cast<uint2*>(P.dv + o) = pv;
+    }
+}
+
+// ---- dQ ----------------------------------------------------------------------------------------
+// Workgroup: 4 waves = queries 128 qt .. 128 qt + 127 of (b, hq); wave w owns queries 32(4qt + w) + [0, 32).
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams P) {
+  __shared__ __align__(16) uint16_t sK[32 * BW_ROW], sV[32 * BW_ROW], sKt[128 * BW_TROW];
+  const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int hk = hq / (P.Hq / P.Hkv);
+  const int qb = 4 * qt + wave, q0 = 32 * qb;
+  const bool valid = q0 < S;
+  const int64_t bhq = (int64_t)b * P.Hq + hq, bhk = (int64_t)b * P.Hkv + hk;
+  // This wave's Q and dO rows as B operands: lane (query c, h), step s holds columns 16s + 8h + [0, 8).
+  v8bf qop[8], gop[8];
+  const int qrow = valid ? q0 + c : 0;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qop[s] = ld8bf(P.qd + (bhq * S + qrow) * 128 + 16 * s + 8 * h);
+    gop[s] = ld8bf(P.gd + (bhq * S + qrow) * 128 + 16 * s + 8 * h);
+  }
+  const float lse2 = P.lse[bhq * S + qrow] * 1.4426950408889634f, del = P.delta[bhq * S + qrow];
+  v16f dqT[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqT[dt][i] = 0.f;
+  const uint16_t *kd = P.kd + bhk * S * 128, *vd = P.vd + bhk * S * 128, *kdt = P.kdt + bhk * 128 * S;
+  const int kb_end = min(4 * qt + 3, S / 32 - 1);  // last key block any wave of the workgroup needs
+  for (int kb = 0; kb <= kb_end; ++kb) {
+    const int k0 = 32 * kb;
+    stage_rows(sK, kd, k0, tid);
+    stage_rows(sV, vd, k0, tid);
+    stage_cols(sKt, kdt, S, k0, tid);
+    __syncthreads();
+    if (valid && kb <= qb) {
+      // S^T = K Q^T and dP^T = V dO^T: lane (query c, h), element i <-> key 8(i/4) + 4h + i%4 of the block
+      v16f sacc, pacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sacc = mfma_bf16(ld8bf(sK + c * BW_ROW + 16 * s + 8 * h), qop[s], sacc);
+        pacc = mfma_bf16(ld8bf(sV + c * BW_ROW + 16 * s + 8 * h), gop[s], pacc);
+      }
+      const bool diag = kb == qb;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lse2));
+        if (diag && kk > c) p = 0.f;
+        pacc[i] = p * (pacc[i] - del);  // dS^T
+      }
+      // dQ^T += K^T dS^T over the 32 keys, two 16-key steps (slot order as in the dK/dV kernel)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const v8bf sb = to_bf16(pacc, t);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 32 * dt + c;
+          const v8bf ka = ld4x2bf(sKt + d * BW_TROW + 16 * t + 4 * h, sKt + d * BW_TROW + 16 * t + 8 + 4 * h);
+          dqT[dt] = mfma_bf16(ka, sb, dqT[dt]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!valid) return;
+  const int64_t off = b * P.qsb + (int64_t)(q0 + c) * P.qss + hq * P.qsh + 4 * h;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      uint2 pq;
+      pq.x = f32_to_bf16(dqT[dt][4 * g4] * P.scale) | (f32_to_bf16(dqT[dt][4 * g4 + 1] * P.scale) << 16);
+      pq.y = f32_to_bf16(dqT[dt][4 * g4 + 2] * P.scale) | (f32_to_bf16(dqT[dt][4 * g4 + 3] * P.scale) << 16);
+      *reinterpret_cast<uint2*>(P.dq + off + 32 * dt + 8 * g4) = pq;
+    }
+}
+
+hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                           const uint8_t* vt, const uint8_t* vta, const uint16_t* o, const float* lse,
+                           const uint16_t* dout, int B, int S, int Hq, int Hkv, float softmax_scale, int64_t qsb,
+                           int64_t qss, int64_t qsh, int64_t ksb, int64_t kss, int64_t ksh, const BwdWorkspace& ws,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream) {
+  const dim3 tq((unsigned)((S + 63) / 64), (unsigned)Hq, (unsigned)B), tk((unsigned)((S + 63) / 64), (unsigned)Hkv,
+                                                                          (unsigned)B);
+  bwd_prep_kernel<0><<<tq, 256, 0, stream>>>(qc, qs, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hq, ws.qd, ws.qdt, nullptr);
+  bwd_prep_kernel<0><<<tk, 256, 0, stream>>>(kc, ks, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.kd, ws.kdt, nullptr);
+  bwd_prep_kernel<1><<<tk, 256, 0, stream>>>(vt, vta, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.vd, nullptr,
+                                             nullptr);
+  bwd_prep_kernel<2><<<tq, 256, 0, stream>>>(nullptr, nullptr, dout, qsb, qss, qsh, o, qsb, qss, qsh, S, Hq, ws.gd,
+                                             ws.gdt, ws.delta);
+  BwdParams p{};
+  p.qd = ws.qd; p.qdt = ws.qdt; p.kd = ws.kd; p.kdt = ws.kdt; p.vd = ws.vd; p.gd = ws.gd; p.gdt = ws.gdt;
+  p.lse = lse; p.delta = ws.delta;
+  p.S = S; p.Hq = Hq; p.Hkv = Hkv;
+  p.scale = softmax_scale;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.qsb = qsb; p.qss = qss; p.qsh = qsh; p.ksb = ksb; p.kss = kss; p.ksh = ksh;
+  const unsigned tiles = (unsigned)((S + 127) / 128);
+  bwd_dkdv_kernel<<<dim3(tiles, (unsigned)Hkv, (unsigned)B), 256, 0, stream>>>(p);
+  bwd_dq_kernel<<<dim3(tiles, (unsigned)Hq, (unsigned)B), 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace mxfa

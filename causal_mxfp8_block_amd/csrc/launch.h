@@ -5,6 +5,13 @@
 
 namespace mxfa {
 
+// Workspace parts of the backward: decoded bf16 operands, head-major, and the transposed copies.
+struct BwdWorkspace {
+  uint16_t *qd, *qdt, *kd, *kdt, *vd, *gd, *gdt;  // [B,H,S,128] and [B,H,128,S]
+  float* delta;                                     // [B,Hq,S]
+  size_t bytes;
+};
+
 hipError_t launch_quantize_rowwise(const uint16_t* x, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
                                    uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_quantize_v(const uint16_t* v, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
@@ -22,6 +29,11 @@ hipError_t launch_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t
                              const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, float softmax_scale,
                              void* out, int64_t osb, int64_t oss, int64_t osh, int out_bf16, float* lse_out,
                              hipStream_t stream);
+hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                           const uint8_t* vt, const uint8_t* vta, const uint16_t* o, const float* lse,
+                           const uint16_t* dout, int B, int S, int Hq, int Hkv, float softmax_scale, int64_t qsb,
+                           int64_t qss, int64_t qsh, int64_t ksb, int64_t kss, int64_t ksh, const BwdWorkspace& ws,
+                           uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream);
 hipError_t launch_attn_own_block(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                  const uint8_t* vt, const uint8_t* vta, int B, int S, int Hq, int Hkv,
                                  float softmax_scale, float* o_o, float* lse_o, hipStream_t stream);

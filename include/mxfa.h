@@ -148,6 +148,28 @@ int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const vo
                   int D, float softmax_scale, void* workspace, size_t workspace_bytes, void* out, int64_t osb,
                   int64_t oss, int64_t osh, int out_dtype, float* lse_out, void* stream);
 
+/* Bytes of workspace mxfa_attn_bwd needs (decoded operands: 5 bf16 copies of [B,Hq,S,D] and 3 of
+ * [B,Hkv,S,D], plus [B,Hq,S] fp32; 256-byte aligned parts). */
+size_t mxfa_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D);
+
+/* attn_bwd -- backward on decoded operands (TE #3865, Description, backward bullet: BF16 backward on
+ * Q/K decoded from their rowwise MXFP8 bytes and V decoded from the token-normalised copy, so no
+ * gradient depends on a later token through a shared scale). The gradients of causal softmax
+ * attention at those operands, with the forward's O and lse as the softmax statistics:
+ *   Delta_i = dO_i . O_i,  P_ij = exp(softmax_scale Q_i . K_j - lse_i) (j <= i),
+ *   dS_ij = P_ij (dO_i . V_j - Delta_i),  dQ_i = softmax_scale sum_j dS_ij K_j,
+ *   dK_j = softmax_scale sum_i dS_ij Q_i,  dV_j = sum_i P_ij dO_i  (dK, dV summed over the query heads
+ *   of a KV head),
+ * computed with bf16 operands (P and dS rounded to bf16 before their products) and fp32 accumulation.
+ * Inputs: the rowwise Q/K codes and the token-normalised V codes (layouts above); o and dout bf16
+ * [B,S,Hq,D] views and dq the bf16 output, all three with the strides (qsb, qss, qsh); dk and dv bf16
+ * [B,S,Hkv,D] outputs with the strides (ksb, kss, ksh); lse fp32 [B,Hq,S] (natural log, as the forward
+ * writes it). workspace: at least mxfa_attn_bwd_workspace_bytes, 256-byte aligned. */
+int mxfa_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
+                  const uint8_t* vta, const void* o, const float* lse, const void* dout, int B, int S, int Hq, int Hkv,
+                  int D, float softmax_scale, int64_t qsb, int64_t qss, int64_t qsh, int64_t ksb, int64_t kss,
+                  int64_t ksh, void* workspace, size_t workspace_bytes, void* dq, void* dk, void* dv, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

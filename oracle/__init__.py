@@ -51,9 +51,9 @@ def _load():
         lib.orc_e4m3_decode.restype = D
         lib.orc_quantize_rowwise.argtypes = [P, I, I, I, I, I64, I64, I64, P, P]
         lib.orc_quantize_rows_f64.argtypes = [P, I64, I, P, P]
-        lib.orc_attn_bwd_values.argtypes = [P] * 6 + [I, I, I, I, I, D, P, I, P, I, P, P, P]
+        lib.orc_attn_bwd_values.argtypes = [P] * 6 + [I, I, I, I, I, D, P, I, P, I, P, P, P, P, P, P]
         lib.orc_attn_bwd.argtypes = [P] * 7 + [I64, I64, I64, P, P, I64, I64, I64, I, I, I, I, I, F, P, I, P, I,
-                                                P, P, P]
+                                                P, P, P, P, P, P]
         lib.orc_quantize_v.argtypes = [P, I, I, I, I, I64, I64, I64, P, P, P, P]
         six = [P] * 6
         lib.orc_attn_completed.argtypes = six + [I, I, I, I, I, F, P, I, I, P, P, D, P, P, D, ctypes.c_uint64]
@@ -318,10 +318,11 @@ def forward_leaky(q, k, v, scale, rows=None, quant: Quantized | None = None, all
     return attn_leaky(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, qv.H, kv.H, scale, rows, allowance=allowance)
 
 
-def attn_bwd_values(Q, K, V, O, dO, lse, scale, qrows=None, krows=None):
+def attn_bwd_values(Q, K, V, O, dO, lse, scale, qrows=None, krows=None, allowance=False):
     """Backward of causal softmax attention at real-valued operands (Q, O, dO [B,Hq,S,D]; K, V
     [B,Hkv,S,D]; lse [B,Hq,S] natural log): (dq [B,Hq,nq,D], dk, dv [B,Hkv,nk,D]) for the query rows
-    ``qrows`` and key rows ``krows`` (None: all rows)."""
+    ``qrows`` and key rows ``krows`` (None: all rows). With ``allowance`` also (aq, ak, av): reading
+    R16, the per-element bound of the bf16 rounding of P and dS as product operands."""
     arrs = [np.ascontiguousarray(a, dtype=np.float64) for a in (Q, K, V, O, dO, lse)]
     B, Hq, S, D = arrs[0].shape
     Hkv = arrs[1].shape[1]
@@ -330,15 +331,17 @@ def attn_bwd_values(Q, K, V, O, dO, lse, scale, qrows=None, krows=None):
     dq = np.empty((B, Hq, nq, D))
     dk = np.empty((B, Hkv, nk, D))
     dv = np.empty((B, Hkv, nk, D))
+    al = [np.empty_like(x) for x in (dq, dk, dv)] if allowance else [None, None, None]
     _load().orc_attn_bwd_values(*[_ptr(a) for a in arrs], B, S, Hq, Hkv, D, float(scale), _ptr(qr), nq, _ptr(kr), nk,
-                                _ptr(dq), _ptr(dk), _ptr(dv))
-    return dq, dk, dv
+                                _ptr(dq), _ptr(dk), _ptr(dv), *[_ptr(a) for a in al])
+    return (dq, dk, dv, *al) if allowance else (dq, dk, dv)
 
 
-def attn_bwd(qc, qs, kc, ks, vt, vta, o, lse, do, scale, qrows=None, krows=None):
+def attn_bwd(qc, qs, kc, ks, vt, vta, o, lse, do, scale, qrows=None, krows=None, allowance=False):
     """Backward on decoded operands from the codes (Q/K rowwise [B,H,S,D] + scales, V token-normalised
     [B,Hkv,S,D] + amplitudes [B,Hkv,S]), the forward's O (bf16 view), lse (fp32 [B,Hq,S]) and the
-    output gradient dO (bf16 view): (dq [B,Hq,nq,D], dk, dv [B,Hkv,nk,D]) in fp64."""
+    output gradient dO (bf16 view): (dq [B,Hq,nq,D], dk, dv [B,Hkv,nk,D]) in fp64, and with
+    ``allowance`` the R16 bounds (aq, ak, av) as attn_bwd_values."""
     ov, gv = _as_view(o), _as_view(do)
     B, Hq, S, D = qc.shape
     Hkv = kc.shape[1]
@@ -347,9 +350,10 @@ def attn_bwd(qc, qs, kc, ks, vt, vta, o, lse, do, scale, qrows=None, krows=None)
     dq = np.empty((B, Hq, nq, D))
     dk = np.empty((B, Hkv, nk, D))
     dv = np.empty((B, Hkv, nk, D))
+    al = [np.empty_like(x) for x in (dq, dk, dv)] if allowance else [None, None, None]
     args = [np.ascontiguousarray(a) for a in (qc, qs, kc, ks, vt, vta)]
     l32 = np.ascontiguousarray(lse, dtype=np.float32)
     _load().orc_attn_bwd(*[_ptr(a) for a in args], _ptr(ov.data), ov.sb, ov.ss, ov.sh, _ptr(l32), _ptr(gv.data), gv.sb,
                          gv.ss, gv.sh, B, S, Hq, Hkv, D, float(scale), _ptr(qr), nq, _ptr(kr), nk, _ptr(dq), _ptr(dk),
-                         _ptr(dv))
-    return dq, dk, dv
+                         _ptr(dv), *[_ptr(a) for a in al])
+    return (dq, dk, dv, *al) if allowance else (dq, dk, dv)

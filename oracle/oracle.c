@@ -582,11 +582,17 @@ void orc_attn_identity(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh,
      dV_j    = sum_{hq of kv head} sum_{i >= j} P_ij dO_i
    Q, O, dO [B,Hq,S,D], K, V [B,Hkv,S,D], lse [B,Hq,S]. dq for the query rows
    qrows (nq of them; NULL: all S) into [B,Hq,nq,D]; dk and dv for the key rows
-   krows (nk; NULL: all) into [B,Hkv,nk,D]. Any output may be NULL. */
+   krows (nk; NULL: all) into [B,Hkv,nk,D]. Any output may be NULL.
+   aq, ak, av (optional, shaped as dq, dk, dv): reading R16, the bf16 backward's
+   operand rounding -- P and dS enter their products rounded to bf16 (relative
+   error at most 2^-8, bf16's unit roundoff) -- bounded per element: aq = 2^-8
+   scale sum_j |dS_ij| |K_j|, ak = 2^-8 scale sum_i |dS_ij| |Q_i|, av = 2^-8
+   sum_i P_ij |dO_i|. */
 void orc_attn_bwd_values(const double* Q, const double* K, const double* V, const double* O, const double* dO,
                          const double* lse, int B, int S, int Hq, int Hkv, int D, double scale,
                          const int32_t* qrows, int nq, const int32_t* krows, int nk, double* dq, double* dk,
-                         double* dv) {
+                         double* dv, double* aq, double* ak, double* av) {
+  const double u = ldexp(1.0, -8);
   const int G = Hq / Hkv;
   double* delta = (double*)malloc(sizeof(double) * (int64_t)B * Hq * S);
 #pragma omp parallel for schedule(static)
@@ -601,13 +607,20 @@ void orc_attn_bwd_values(const double* Q, const double* K, const double* V, cons
           const double* Kh = K + ((int64_t)b * Hkv + hk) * S * D;
           const double* Vh = V + ((int64_t)b * Hkv + hk) * S * D;
           double* out = dq + (((int64_t)b * Hq + hq) * nq + r) * D;
+          double* al = aq ? aq + (((int64_t)b * Hq + hq) * nq + r) * D : NULL;
           for (int d = 0; d < D; ++d) out[d] = 0.0;
+          if (al)
+            for (int d = 0; d < D; ++d) al[d] = 0.0;
           for (int j = 0; j <= i; ++j) {
             const double p = exp(scale * dot(Q + qi * D, Kh + (int64_t)j * D, D) - lse[qi]);
             const double ds = p * (dot(dO + qi * D, Vh + (int64_t)j * D, D) - delta[qi]);
             for (int d = 0; d < D; ++d) out[d] += ds * Kh[(int64_t)j * D + d];
+            if (al)
+              for (int d = 0; d < D; ++d) al[d] += fabs(ds * Kh[(int64_t)j * D + d]);
           }
           for (int d = 0; d < D; ++d) out[d] *= scale;
+          if (al)
+            for (int d = 0; d < D; ++d) al[d] *= u * scale;
         }
   }
   if (dk || dv) {
@@ -618,25 +631,33 @@ void orc_attn_bwd_values(const double* Q, const double* K, const double* V, cons
           const int j = row_index(krows, r);
           const double* kj = K + (((int64_t)b * Hkv + hk) * S + j) * D;
           const double* vj = V + (((int64_t)b * Hkv + hk) * S + j) * D;
-          double* ak = (double*)calloc(D, sizeof(double));
-          double* av = (double*)calloc(D, sizeof(double));
+          double* ak_ = (double*)calloc(D, sizeof(double));
+          double* av_ = (double*)calloc(D, sizeof(double));
+          double* bk = (double*)calloc(D, sizeof(double));
+          double* bv = (double*)calloc(D, sizeof(double));
           for (int hq = hk * G; hq < (hk + 1) * G; ++hq)
             for (int i = j; i < S; ++i) {
               const int64_t qi = (((int64_t)b * Hq + hq) * S + i);
               const double p = exp(scale * dot(Q + qi * D, kj, D) - lse[qi]);
               const double ds = p * (dot(dO + qi * D, vj, D) - delta[qi]);
               for (int d = 0; d < D; ++d) {
-                av[d] += p * dO[qi * D + d];
-                ak[d] += ds * Q[qi * D + d];
+                av_[d] += p * dO[qi * D + d];
+                ak_[d] += ds * Q[qi * D + d];
+                bv[d] += fabs(p * dO[qi * D + d]);
+                bk[d] += fabs(ds * Q[qi * D + d]);
               }
             }
           const int64_t orow = (((int64_t)b * Hkv + hk) * nk + r) * D;
           for (int d = 0; d < D; ++d) {
-            if (dk) dk[orow + d] = scale * ak[d];
-            if (dv) dv[orow + d] = av[d];
+            if (dk) dk[orow + d] = scale * ak_[d];
+            if (dv) dv[orow + d] = av_[d];
+            if (ak) ak[orow + d] = u * scale * bk[d];
+            if (av) av[orow + d] = u * bv[d];
           }
-          free(ak);
-          free(av);
+          free(ak_);
+          free(av_);
+          free(bk);
+          free(bv);
         }
   }
   free(delta);
@@ -649,7 +670,7 @@ void orc_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const
                   const uint8_t* vta, const uint16_t* o, int64_t osb, int64_t oss, int64_t osh, const float* lse,
                   const uint16_t* dout, int64_t gsb, int64_t gss, int64_t gsh, int B, int S, int Hq, int Hkv, int D,
                   float scale, const int32_t* qrows, int nq, const int32_t* krows, int nk, double* dq, double* dk,
-                  double* dv) {
+                  double* dv, double* aq, double* ak, double* av) {
   double* Q = decode_rowwise(qc, qs, B, Hq, S, D);
   double* K = decode_rowwise(kc, ks, B, Hkv, S, D);
   double* V = decode_vtn(vt, vta, B, Hkv, S, D);
@@ -657,7 +678,8 @@ void orc_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const
   double* dOv = bf16_tensor(dout, gsb, gss, gsh, B, S, Hq, D);
   double* L = (double*)malloc(sizeof(double) * (int64_t)B * Hq * S);
   for (int64_t r = 0; r < (int64_t)B * Hq * S; ++r) L[r] = (double)lse[r];
-  orc_attn_bwd_values(Q, K, V, Ov, dOv, L, B, S, Hq, Hkv, D, (double)scale, qrows, nq, krows, nk, dq, dk, dv);
+  orc_attn_bwd_values(Q, K, V, Ov, dOv, L, B, S, Hq, Hkv, D, (double)scale, qrows, nq, krows, nk, dq, dk, dv, aq,
+                      ak, av);
   free(Q);
   free(K);
   free(V);

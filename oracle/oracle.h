@@ -98,16 +98,17 @@ void orc_attn_identity(const uint16_t* q, int64_t qsb, int64_t qss, int64_t qsh,
 }
 #endif
 /* Backward on decoded operands: real-valued form (dq for query rows qrows,
-   dk/dv for key rows krows; NULL row lists mean all rows; outputs may be NULL). */
+   dk/dv for key rows krows; NULL row lists mean all rows; outputs may be NULL;
+   aq, ak, av: the bf16 operand-rounding bound of each, reading R16). */
 void orc_attn_bwd_values(const double* Q, const double* K, const double* V, const double* O, const double* dO,
                          const double* lse, int B, int S, int Hq, int Hkv, int D, double scale,
                          const int32_t* qrows, int nq, const int32_t* krows, int nk, double* dq, double* dk,
-                         double* dv);
+                         double* dv, double* aq, double* ak, double* av);
 /* The same from codes (Q, K rowwise; V token-normalised) and bf16 O, dO views. */
 void orc_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vt,
                   const uint8_t* vta, const uint16_t* o, int64_t osb, int64_t oss, int64_t osh, const float* lse,
                   const uint16_t* dout, int64_t gsb, int64_t gss, int64_t gsh, int B, int S, int Hq, int Hkv, int D,
                   float scale, const int32_t* qrows, int nq, const int32_t* krows, int nk, double* dq, double* dk,
-                  double* dv);
+                  double* dv, double* aq, double* ak, double* av);
 
 #endif

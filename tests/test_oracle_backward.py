@@ -96,3 +96,30 @@ def test_codes_entry_equals_values_entry_on_decoded_operands():
     h = oracle.attn_bwd_values(Qd, Kd, Vd, to(o), to(do), lse.astype(np.float64), float(np.float32(scale)))
     for a, b in zip(g, h):
         assert np.array_equal(a, b)
+
+
+def test_bf16_rounding_allowance_covers_rounded_operands():
+    """R16 pin: gradients computed with P and dS rounded to bf16 before their products (a model of
+    the bf16 kernel) differ from the exact ones by at most the allowance, and the allowance is
+    exercised (the rounding moves the gradients)."""
+    rng = np.random.default_rng(44)
+    B, Hq, Hkv, S, D, scale = 1, 2, 1, 96, 128, 0.0884
+    Q, K, V = _rand((B, Hq, S, D), rng), _rand((B, Hkv, S, D), rng), _rand((B, Hkv, S, D), rng) * 4
+    dO = _rand((B, Hq, S, D), rng)
+    O, lse = _forward(Q, K, V, scale)
+    O = O + 0.01 * _rand(O.shape, rng)  # statistics need not be those of Q, K, V exactly
+    dq, dk, dv, aq, ak, av = oracle.attn_bwd_values(Q, K, V, O, dO, lse, scale, allowance=True)
+    G = Hq // Hkv
+    Kr, Vr = np.repeat(K, G, axis=1), np.repeat(V, G, axis=1)
+    p = np.exp(scale * np.einsum("bhid,bhjd->bhij", Q, Kr) - lse[..., None])
+    p = np.where(np.tril(np.ones((S, S), bool)), p, 0.0)
+    delta = np.sum(dO * O, axis=-1)
+    ds = p * (np.einsum("bhid,bhjd->bhij", dO, Vr) - delta[..., None])
+    rb = lambda x: bf16_to_f32(bf16_bits(x.astype(np.float32))).astype(np.float64)
+    pb, dsb = rb(p), rb(ds)
+    mq = scale * np.einsum("bhij,bhjd->bhid", dsb, Kr)
+    mk = scale * np.einsum("bhij,bhid->bhjd", dsb, Q).reshape(B, Hkv, G, S, D).sum(axis=2)
+    mv = np.einsum("bhij,bhid->bhjd", pb, dO).reshape(B, Hkv, G, S, D).sum(axis=2)
+    for m, ref, al in ((mq, dq, aq), (mk, dk, ak), (mv, dv, av)):
+        assert np.all(np.abs(m - ref) <= al * (1 + 1e-9) + 1e-12)
+        assert np.max(np.abs(m - ref)) > 0
