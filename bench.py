@@ -36,6 +36,11 @@ HBM_PEAK_GBS = 8000.0
 # Published own-block forward time for this workload (B200, includes quantisation): 2.797 ms,
 # i.e. 2*1*16*32768^2*128 / 2.797 ms = 1572.4 TFLOP/s. Context from other hardware, not a target.
 PAGES_TFLOPS = 2 * 16 * 32768 ** 2 * 128 / 2.797e-3 / 1e12
+# Published own-block forward+backward for B=1, 16/16 heads, S=32768 (B200): 12.799 ms; with the
+# FlashAttention count (backward = 2.5 x forward) that is 3.5 * 2*16*32768^2*128 / 12.799 ms.
+METRIC_FWDBWD = "causal MXFP8 attn fwd + bf16 bwd TFLOP/s + ms at B=1,H=16/16,S=32K,D=128 SBHD"
+PAGES_FWDBWD_TFLOPS = 3.5 * 2 * 16 * 32768 ** 2 * 128 / 12.799e-3 / 1e12
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
 def completed_pairs(B, Hq, S):
@@ -97,6 +102,9 @@ def main():
                     help="fused (default): the leak-free forward in one attention kernel; stepwise: its three "
                          "separate kernels; leaky: ordinary causal MXFP8 (the variant the method replaces)")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle CPU-baseline sample (0 skips)")
+    ap.add_argument("--mode", choices=["fwd", "fwdbwd"], default="fwd",
+                    help="fwd (default): the forward metric; fwdbwd: forward + bf16 backward on decoded operands "
+                         "(default workload mha16_s32k_sbhd, the configuration the published fwd+bwd times use)")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the calibration for HBM counters")
     args = ap.parse_args()
@@ -118,6 +126,8 @@ def main():
     import causal_mxfp8_block_amd as mx
     from causal_mxfp8_block_amd.inputs import WORKLOADS, make_inputs
 
+    if args.mode == "fwdbwd":
+        return run_fwdbwd(args, torch, mx, WORKLOADS, make_inputs)
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
     dev = torch.device("cuda:0")
@@ -250,6 +260,73 @@ def main():
     }
     if args.cpu_rows > 0 and not leaky:  # the baseline times the oracle of the leak-free path
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+def run_fwdbwd(args, torch, mx, WORKLOADS, make_inputs):
+    """One step = quantise Q, K, V; fused forward; backward on decoded operands (its preparation,
+    dK/dV and dQ kernels) for a seeded dO. Prints one JSON line."""
+    name = "mha16_s32k_sbhd" if args.workload == "gqa16x4_s32k_amplitudes" else args.workload
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = to(inp.q), to(inp.k), to(inp.v)
+    rng = np.random.default_rng(w.seed + 1)
+    g = torch.from_numpy(rng.standard_normal(inp.q.shape).astype(np.float32)).to(dev).to(torch.bfloat16)
+    lay, B, S, Hq, Hkv, D = w.layout, w.B, w.S, w.Hq, w.Hkv, w.D
+    stream = torch.cuda.current_stream(dev)
+    ws_b = torch.empty(int(mx.lib().mxfa_attn_bwd_workspace_bytes(B, S, Hq, Hkv, D)), dtype=torch.uint8, device=dev)
+    names = ["quantize", "forward", "backward"]
+
+    def step(evs=None):
+        def rec(i, j):
+            if evs is not None:
+                evs[i][j].record(stream)
+        rec(0, 0)
+        qc, qs = mx.mxfp8_quantize(q, "rowwise", lay)
+        kc, ks = mx.mxfp8_quantize(k, "rowwise", lay)
+        vc, vcs, vt, vta = mx.mxfp8_quantize(v, "v", lay)
+        rec(0, 1)
+        rec(1, 0)
+        o, lse = mx.attn_fwd_fused(qc, qs, kc, ks, vc, vcs, vt, vta, w.scale, layout=lay)
+        rec(1, 1)
+        rec(2, 0)
+        mx.attn_bwd(qc, qs, kc, ks, vt, vta, o, lse, g, w.scale, layout=lay, workspace=ws_b)
+        rec(2, 1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {n: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+    fwd_flops = 2.0 * B * Hq * S * S * D
+    value = 3.5 * fwd_flops / (ms_step * 1e-3) / 1e12
+    # algorithmic backward work: 5 products of 2*D FLOP (S, dP, dV, dK, dQ) per (query, visible key) pair
+    bwd_alg = 1280.0 * (completed_pairs(B, Hq, S) + own_pairs(B, Hq, S))
+    res = {
+        "metric": METRIC_FWDBWD, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": round(value / PAGES_FWDBWD_TFLOPS, 4) if w.name == "mha16_s32k_sbhd" else None,
+        "dtype": "mxfp8 fwd / bf16 bwd", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "layout": lay, "causal": True,
+                   "values": w.values, "flop_count": "FlashAttention convention: fwd 2BHS^2D, bwd 2.5x fwd"},
+        "roofline": {"bound": "mfma", "achieved": round(bwd_alg / (per["backward"] * 1e-3) / 1e12, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_alg / (per["backward"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "backward (preparation + dK/dV + dQ kernels, bf16 MFMA)",
+                     "launch_ms": round(per["backward"], 4)},
+        "kernels": {n: {"ms": round(per[n], 4)} for n in names},
+        "cpu_baseline": None,
+    }
     print(json.dumps(res), flush=True)
 
 
