@@ -11,28 +11,56 @@ LIB = os.path.join(PKG, "libmxfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden", "-Wall",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
     # packed fp32 ops stay off: scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source extra flags. The backward kernels run one or two waves per SIMD, so their LDS operand reads
+# must be issued well ahead of the MFMAs that use them: the ILP-first machine scheduler does that, the
+# default occupancy-first one sinks each read next to its use.
+EXTRA = {"attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip"))) + [os.path.join(PKG, "csrc", "api.cpp")]
 
 
+def _clean(stderr: str) -> str:
+    noise = "is not a recognized feature for this target"
+    return "\n".join(l for l in (stderr or "").splitlines() if noise not in l)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 into causal_mxfp8_block_amd/libmxfa.so (always rebuilds)."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
-    os.replace(tmp, LIB)
+    tag = f".tmp{os.getpid()}"
+    inc = ["-I", os.path.join(ROOT, "include")]
+    objs, procs = [], []
+    for src in sources():  # one object per source (own flags), compiled in parallel, then one link
+        obj = os.path.join(PKG, "csrc", os.path.basename(src) + tag + ".o")
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), *inc, "-c", "-o", obj, src]
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    errs = []
+    try:
+        for src, pr in procs:
+            _, stderr = pr.communicate()
+            err = _clean(stderr)
+            if pr.returncode != 0:
+                errs.append(f"{os.path.basename(src)}: hipcc failed ({pr.returncode}):\n{err}")
+            elif verbose and err.strip():
+                print(err)
+        if errs:
+            raise RuntimeError("\n".join(errs))
+        tmp = LIB + tag
+        res = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed ({res.returncode}):\n{_clean(res.stderr)}")
+        os.replace(tmp, LIB)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return LIB
 
 

@@ -21,9 +21,12 @@
 //  * dQ kernel: one wave per 32 queries, their Q and dO operands in registers. For every 32-key block
 //    at or before the queries it computes S^T = K Q^T and dP^T = V dO^T (queries on the lanes: lse and
 //    Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way.
-//  * The 32-token blocks on the diagonal mask key > query; blocks beyond it are skipped.
-//  * Query (dK/dV) and key (dQ) blocks are staged in LDS per workgroup of 4 waves, rows padded so
-//    that the 16- and 8-byte operand reads are bank-conflict-free.
+//  * Key > query is masked to P = 0. The loops start at the workgroup's first block on or below the
+//    diagonal, so a wave whose own blocks start later computes at most three fully masked steps; that
+//    keeps the loop branch-free per wave.
+//  * Query (dK/dV) and key (dQ) blocks are staged in LDS per workgroup of 4 waves, double-buffered
+//    (the next step's tiles are fetched into registers while the current one computes), rows
+//    padded so that the 16- and 8-byte operand reads are bank-conflict-free.
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,15 +35,13 @@ namespace mxfa {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BW_ROW = 136;  // LDS pitch (bf16) of a [token][D] tile row: 128 + 8 pad
-constexpr int BW_TROW = 36;  // LDS pitch (bf16) of a [D][32 tokens] tile row: 32 + 4 pad
+// LDS pitch (bf16) of a [D][32 tokens] tile row: 32 + 8 pad (rows 16-byte aligned, conflict-free 16-byte
+// reads). Within each 16-token group the tokens are stored in MFMA slot order: token u at position u with
+// bits 2 and 3 swapped, so one 16-byte read at 8h gives tokens 4h..4h+3 and 8+4h..8+4h+3.
+constexpr int BW_TROW = 40;
 
 __device__ __forceinline__ v8bf ld8bf(const uint16_t* p) {  // 16 bytes, 16-byte aligned
   return __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(p));
-}
-// Two 8-byte halves (4 bf16 each) into one operand.
-__device__ __forceinline__ v8bf ld4x2bf(const uint16_t* p0, const uint16_t* p1) {
-  const uint2 a = *reinterpret_cast<const uint2*>(p0), b = *reinterpret_cast<const uint2*>(p1);
-  return __builtin_bit_cast(v8bf, make_uint4(a.x, a.y, b.x, b.y));
 }
 __device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -144,32 +145,43 @@ struct BwdParams {
   int64_t qsb, qss, qsh, ksb, kss, ksh;                 // strides of dq and of dk/dv
 };
 
-// Stage a 32-token x 128 row-major block (src rows t0..t0+31 of a [S][128] bf16 head) into LDS.
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int t0, int tid) {
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int idx = tid + 256 * r, row = idx >> 4, col = (idx & 15) * 8;
-    *reinterpret_cast<uint4*>(dst + row * BW_ROW + col) =
-        *reinterpret_cast<const uint4*>(src + (int64_t)(t0 + row) * 128 + col);
-  }
+// Tile staging, split into the global loads (into registers, issued a step ahead) and the LDS stores.
+// Thread tid moves two 16-byte pieces i = 0, 1 of each tile.
+// Rows: a 32-token x 128 block (rows t0..t0+31 of a [S][128] bf16 head).
+__device__ __forceinline__ uint4 load_row16(const uint16_t* src, int t0, int tid, int i) {
+  const int idx = tid + 256 * i, row = idx >> 4, col = (idx & 15) * 8;
+  return *reinterpret_cast<const uint4*>(src + (int64_t)(t0 + row) * 128 + col);
 }
-// Stage the 128 x 32-token block (columns t0..t0+31 of a [128][S] transposed head) into LDS.
-__device__ __forceinline__ void stage_cols(uint16_t* dst, const uint16_t* src, int S, int t0, int tid) {
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int idx = tid + 256 * r, d = idx >> 2, col = (idx & 3) * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)d * S + t0 + col);
-    uint2* p = reinterpret_cast<uint2*>(dst + d * BW_TROW + col);  // rows are 8-byte aligned
-    p[0] = make_uint2(v.x, v.y);
-    p[1] = make_uint2(v.z, v.w);
-  }
+__device__ __forceinline__ void store_row16(uint16_t* dst, uint4 v, int tid, int i) {
+  const int idx = tid + 256 * i, row = idx >> 4, col = (idx & 15) * 8;
+  *reinterpret_cast<uint4*>(dst + row * BW_ROW + col) = v;
+}
+// Columns: the 128 x 32-token block (columns t0..t0+31 of a [128][S] transposed head).
+__device__ __forceinline__ uint4 load_col16(const uint16_t* src, int S, int t0, int tid, int i) {
+  const int idx = tid + 256 * i, d = idx >> 2, col = (idx & 3) * 8;
+  return *reinterpret_cast<const uint4*>(src + (int64_t)d * S + t0 + col);
+}
+__device__ __forceinline__ void store_col16(uint16_t* dst, uint4 v, int tid, int i) {
+  // tokens col..col+3 and col+4..col+7 (col % 8 == 0) go to their slot-order positions
+  const int idx = tid + 256 * i, d = idx >> 2, col = (idx & 3) * 8;
+  const int lo = (col & 16) + ((col & 8) >> 1);
+  uint16_t* row = dst + d * BW_TROW;
+  *reinterpret_cast<uint2*>(row + lo) = make_uint2(v.x, v.y);
+  *reinterpret_cast<uint2*>(row + lo + 8) = make_uint2(v.z, v.w);
 }
 
 // ---- dK, dV ------------------------------------------------------------------------------------
 // Workgroup: 4 waves = keys 128 kt .. 128 kt + 127 of (b, hk); wave w owns keys 32(4kt + w) + [0, 32).
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams P) {
-  __shared__ __align__(16) uint16_t sQ[32 * BW_ROW], sG[32 * BW_ROW], sQt[128 * BW_TROW], sGt[128 * BW_TROW];
-  __shared__ __align__(16) float sL[32], sD[32];
+// Steps n = (query head, 32-query block), the blocks from the last one down to 4kt: workgroups that run
+// together then read the same query block at the same time, and all but the first take it from L2. The
+// tiles of step n+1 are fetched into registers while step n computes from its LDS buffer, then stored
+// into the other buffer.
+struct DkdvTiles {
+  uint16_t q[32 * BW_ROW], g[32 * BW_ROW], qt[128 * BW_TROW], gt[128 * BW_TROW];
+  float l[32], d[32];
+};
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams P) {
+  __shared__ __align__(16) DkdvTiles buf[2];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
   const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int G = P.Hq / P.Hkv;
@@ -189,66 +201,119 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams P) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
-  const int nqb = S / 32;
-  for (int hq = hk * G; hq < (hk + 1) * G; ++hq) {
-    const int64_t bhq = (int64_t)b * P.Hq + hq;
-    const uint16_t *qd = P.qd + bhq * S * 128, *gd = P.gd + bhq * S * 128;
-    const uint16_t *qdt = P.qdt + bhq * 128 * S, *gdt = P.gdt + bhq * 128 * S;
-    for (int qb = 4 * kt; qb < nqb; ++qb) {
-      const int q0 = 32 * qb;
-      stage_rows(sQ, qd, q0, tid);
-      stage_rows(sG, gd, q0, tid);
-      stage_cols(sQt, qdt, S, q0, tid);
-      stage_cols(sGt, gdt, S, q0, tid);
-      if (tid < 32) {
-        sL[tid] = P.lse[bhq * S + q0 + tid] * 1.4426950408889634f;
-        sD[tid] = P.delta[bhq * S + q0 + tid];
+  const int nqb = S / 32, qb0 = 4 * kt, per_head = nqb - qb0, nsteps = G * per_head;
+  uint4 rq0, rq1, rg0, rg1, rqt0, rqt1, rgt0, rgt1;
+  float rl = 0.f, rd = 0.f;
+  // step n: query head hk*G + n / per_head, query block nqb - 1 - n % per_head
+#define DKDV_FETCH(n)                                                           \
+  do {                                                                          \
+    const int hq_ = hk * G + (n) / per_head, q0_ = 32 * (nqb - 1 - (n) % per_head); \
+    const int64_t bhq_ = (int64_t)b * P.Hq + hq_;                               \
+    const uint16_t *q_ = P.qd + bhq_ * S * 128, *g_ = P.gd + bhq_ * S * 128;    \
+    const uint16_t *qt_ = P.qdt + bhq_ * 128 * S, *gt_ = P.gdt + bhq_ * 128 * S; \
+    rq0 = load_row16(q_, q0_, tid, 0);                                          \
+    rq1 = load_row16(q_, q0_, tid, 1);                                          \
+    rg0 = load_row16(g_, q0_, tid, 0);                                          \
+    rg1 = load_row16(g_, q0_, tid, 1);                                          \
+    rqt0 = load_col16(qt_, S, q0_, tid, 0);                                     \
+    rqt1 = load_col16(qt_, S, q0_, tid, 1);                                     \
+    rgt0 = load_col16(gt_, S, q0_, tid, 0);                                     \
+    rgt1 = load_col16(gt_, S, q0_, tid, 1);                                     \
+    if (tid < 32) {                                                             \
+      rl = P.lse[bhq_ * S + q0_ + tid] * 1.4426950408889634f;                   \
+      rd = P.delta[bhq_ * S + q0_ + tid];                                       \
+    }                                                                           \
+  } while (0)
+#define DKDV_PUT(t)                \
+  do {                             \
+    store_row16(t.q, rq0, tid, 0); \
+    store_row16(t.q, rq1, tid, 1); \
+    store_row16(t.g, rg0, tid, 0); \
+    store_row16(t.g, rg1, tid, 1); \
+    store_col16(t.qt, rqt0, tid, 0); \
+    store_col16(t.qt, rqt1, tid, 1); \
+    store_col16(t.gt, rgt0, tid, 0); \
+    store_col16(t.gt, rgt1, tid, 1); \
+    if (tid < 32) {                \
+      t.l[tid] = rl;               \
+      t.d[tid] = rd;               \
+    }                              \
+  } while (0)
+  DKDV_FETCH(0);
+  DKDV_PUT(buf[0]);
+  __syncthreads();
+  for (int n = 0; n < nsteps; ++n) {
+    if (n + 1 < nsteps) DKDV_FETCH(n + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const DkdvTiles& T = buf[n & 1];
+    const int qb = nqb - 1 - n % per_head;
+    {  // every wave computes every step (branch-free: the accumulators stay in place); masked below
+      // S = Q K^T and dP = dO V^T: lane (key c, h), element i <-> query 8(i/4) + 4h + i%4 of the block
+      // All operand reads of a phase are issued before its MFMAs, so LDS latency is paid once.
+      v8bf qa[8], ga[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        qa[s] = ld8bf(T.q + c * BW_ROW + 16 * s + 8 * h);
+        ga[s] = ld8bf(T.g + c * BW_ROW + 16 * s + 8 * h);
       }
-      __syncthreads();
-      if (valid && qb >= kb) {
-        // S = Q K^T and dP = dO V^T: lane (key c, h), element i <-> query 8(i/4) + 4h + i%4 of the block
-        v16f sacc, pacc;
+      v16f sacc, pacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          sacc = mfma_bf16(ld8bf(sQ + c * BW_ROW + 16 * s + 8 * h), kop[s], sacc);
-          pacc = mfma_bf16(ld8bf(sG + c * BW_ROW + 16 * s + 8 * h), vop[s], pacc);
+      for (int s = 0; s < 8; ++s) {
+        sacc = mfma_bf16(qa[s], kop[s], sacc);
+        pacc = mfma_bf16(ga[s], vop[s], pacc);
+      }
+      // A operands of the dV/dK products (row d = 32dt + c of the transposed tiles, slot order)
+      v8bf gta[2][4], qta[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          gta[t][dt] = ld8bf(T.gt + (32 * dt + c) * BW_TROW + 16 * t + 8 * h);
+          qta[t][dt] = ld8bf(T.qt + (32 * dt + c) * BW_TROW + 16 * t + 8 * h);
         }
-        const bool diag = qb == kb;
+      float4 l4[4], d4[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 l4 = *reinterpret_cast<const float4*>(sL + 8 * g4 + 4 * h);
-          const float4 d4 = *reinterpret_cast<const float4*>(sD + 8 * g4 + 4 * h);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+      for (int g4 = 0; g4 < 4; ++g4) {
+        l4[g4] = *reinterpret_cast<const float4*>(T.l + 8 * g4 + 4 * h);
+        d4[g4] = *reinterpret_cast<const float4*>(T.d + 8 * g4 + 4 * h);
+      }
+      const int qoff = 32 * (qb - kb);  // query - key offset of the two blocks
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e, qq = 8 * g4 + 4 * h + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lv[e]));
-            if (diag && c > qq) p = 0.f;
-            sacc[i] = p;                       // P
-            pacc[i] = p * (pacc[i] - dv[e]);   // dS
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries, two 16-query steps. Step t, B slot
-        // (h, e) is accumulator element 8t + e: query 16t + 8(e/4) + 4h + e%4; the A operand (row d)
-        // reads those queries from the transposed tile.
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float lv[4] = {l4[g4].x, l4[g4].y, l4[g4].z, l4[g4].w};
+        const float dv[4] = {d4[g4].x, d4[g4].y, d4[g4].z, d4[g4].w};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const v8bf pb = to_bf16(sacc, t), sb = to_bf16(pacc, t);
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int d = 32 * dt + c;
-            const v8bf ga = ld4x2bf(sGt + d * BW_TROW + 16 * t + 4 * h, sGt + d * BW_TROW + 16 * t + 8 + 4 * h);
-            const v8bf qa = ld4x2bf(sQt + d * BW_TROW + 16 * t + 4 * h, sQt + d * BW_TROW + 16 * t + 8 + 4 * h);
-            dvT[dt] = mfma_bf16(ga, pb, dvT[dt]);
-            dkT[dt] = mfma_bf16(qa, sb, dkT[dt]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e, qq = 8 * g4 + 4 * h + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lv[e]));
+          if (c > qoff + qq) p = 0.f;  // key after query (whole block when qb < kb)
+          sacc[i] = p;                       // P
+          pacc[i] = p * (pacc[i] - dv[e]);   // dS
         }
       }
-      __syncthreads();
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries, two 16-query steps. Step t, B slot
+      // (h, e) is accumulator element 8t + e: query 16t + 8(e/4) + 4h + e%4, the A operand's slot
+      // order in the transposed tile.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const v8bf pb = to_bf16(sacc, t), sb = to_bf16(pacc, t);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          dvT[dt] = mfma_bf16(gta[t][dt], pb, dvT[dt]);
+          dkT[dt] = mfma_bf16(qta[t][dt], sb, dkT[dt]);
+        }
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 1 < nsteps) DKDV_PUT(buf[(n + 1) & 1]);
+    // Unconditional vmcnt(0): the prefetch registers are free on every path out of the step.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   }
+#undef DKDV_FETCH
+#undef DKDV_PUT
   if (!valid) return;
   // lane (key c, h), element i of tile dt: column 32dt + 8(i/4) + 4h + i%4
   const int64_t off = b * P.ksb + (int64_t)(key0 + c) * P.kss + hk * P.ksh + 4 * h;
@@ -269,8 +334,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams P) {
 
 // ---- dQ ----------------------------------------------------------------------------------------
 // Workgroup: 4 waves = queries 128 qt .. 128 qt + 127 of (b, hq); wave w owns queries 32(4qt + w) + [0, 32).
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams P) {
-  __shared__ __align__(16) uint16_t sK[32 * BW_ROW], sV[32 * BW_ROW], sKt[128 * BW_TROW];
+// Key blocks staged double-buffered as in the dK/dV kernel.
+struct DqTiles {
+  uint16_t k[32 * BW_ROW], v[32 * BW_ROW], kt[128 * BW_TROW];
+};
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams P) {
+  __shared__ __align__(16) DqTiles buf[2];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
   const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int hk = hq / (P.Hq / P.Hkv);
@@ -292,29 +361,60 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams P) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqT[dt][i] = 0.f;
   const uint16_t *kd = P.kd + bhk * S * 128, *vd = P.vd + bhk * S * 128, *kdt = P.kdt + bhk * 128 * S;
-  const int kb_end = min(4 * qt + 3, S / 32 - 1);  // last key block any wave of the workgroup needs
-  for (int kb = 0; kb <= kb_end; ++kb) {
-    const int k0 = 32 * kb;
-    stage_rows(sK, kd, k0, tid);
-    stage_rows(sV, vd, k0, tid);
-    stage_cols(sKt, kdt, S, k0, tid);
-    __syncthreads();
-    if (valid && kb <= qb) {
+  const int nkb = min(4 * qt + 3, S / 32 - 1) + 1;  // key blocks any wave of the workgroup needs
+  uint4 rk0, rk1, rv0, rv1, rkt0, rkt1;
+#define DQ_FETCH(kb)                                \
+  do {                                              \
+    rk0 = load_row16(kd, 32 * (kb), tid, 0);        \
+    rk1 = load_row16(kd, 32 * (kb), tid, 1);        \
+    rv0 = load_row16(vd, 32 * (kb), tid, 0);        \
+    rv1 = load_row16(vd, 32 * (kb), tid, 1);        \
+    rkt0 = load_col16(kdt, S, 32 * (kb), tid, 0);   \
+    rkt1 = load_col16(kdt, S, 32 * (kb), tid, 1);   \
+  } while (0)
+#define DQ_PUT(t)                    \
+  do {                               \
+    store_row16(t.k, rk0, tid, 0);   \
+    store_row16(t.k, rk1, tid, 1);   \
+    store_row16(t.v, rv0, tid, 0);   \
+    store_row16(t.v, rv1, tid, 1);   \
+    store_col16(t.kt, rkt0, tid, 0); \
+    store_col16(t.kt, rkt1, tid, 1); \
+  } while (0)
+  DQ_FETCH(0);
+  DQ_PUT(buf[0]);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) DQ_FETCH(kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const DqTiles& T = buf[kb & 1];
+    {  // branch-free as in the dK/dV kernel
       // S^T = K Q^T and dP^T = V dO^T: lane (query c, h), element i <-> key 8(i/4) + 4h + i%4 of the block
+      v8bf ka[8], va[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        ka[s] = ld8bf(T.k + c * BW_ROW + 16 * s + 8 * h);
+        va[s] = ld8bf(T.v + c * BW_ROW + 16 * s + 8 * h);
+      }
       v16f sacc, pacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sacc = mfma_bf16(ld8bf(sK + c * BW_ROW + 16 * s + 8 * h), qop[s], sacc);
-        pacc = mfma_bf16(ld8bf(sV + c * BW_ROW + 16 * s + 8 * h), gop[s], pacc);
+        sacc = mfma_bf16(ka[s], qop[s], sacc);
+        pacc = mfma_bf16(va[s], gop[s], pacc);
       }
-      const bool diag = kb == qb;
+      v8bf kta[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) kta[t][dt] = ld8bf(T.kt + (32 * dt + c) * BW_TROW + 16 * t + 8 * h);
+      const int qoff = 32 * (qb - kb);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lse2));
-        if (diag && kk > c) p = 0.f;
+        if (kk > qoff + c) p = 0.f;  // key after query (whole block when kb > qb)
         pacc[i] = p * (pacc[i] - del);  // dS^T
       }
       // dQ^T += K^T dS^T over the 32 keys, two 16-key steps (slot order as in the dK/dV kernel)
@@ -322,15 +422,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams P) {
       for (int t = 0; t < 2; ++t) {
         const v8bf sb = to_bf16(pacc, t);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + c;
-          const v8bf ka = ld4x2bf(sKt + d * BW_TROW + 16 * t + 4 * h, sKt + d * BW_TROW + 16 * t + 8 + 4 * h);
-          dqT[dt] = mfma_bf16(ka, sb, dqT[dt]);
-        }
+        for (int dt = 0; dt < 4; ++dt) dqT[dt] = mfma_bf16(kta[t][dt], sb, dqT[dt]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + 1 < nkb) DQ_PUT(buf[(kb + 1) & 1]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
+#undef DQ_FETCH
+#undef DQ_PUT
   if (!valid) return;
   const int64_t off = b * P.qsb + (int64_t)(q0 + c) * P.qss + hq * P.qsh + 4 * h;
 #pragma unroll
