@@ -171,165 +171,180 @@ __device__ __forceinline__ void store_col16(uint16_t* dst, uint4 v, int tid, int
 }
 
 // ---- dK, dV ------------------------------------------------------------------------------------
-// Workgroup: 4 waves = keys 128 kt .. 128 kt + 127 of (b, hk); wave w owns keys 32(4kt + w) + [0, 32).
-// Steps n = (query head, 32-query block), the blocks from the last one down to 4kt: workgroups that run
-// together then read the same query block at the same time, and all but the first take it from L2. The
-// tiles of step n+1 are fetched into registers while step n computes from its LDS buffer, then stored
-// into the other buffer.
+// v_mfma_f32_16x16x32_bf16 (operand layout probed): A lane (m = l%16, g = l/16) element e <-> A[m][8g+e];
+// B lane (n = l%16, g) element e <-> B[8g+e][n]; C lane (n = l%16, g) element i <-> C[4g+i][n].
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f mfma16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Position of query q (0..31) of a transposed dK/dV tile row: MFMA slot order, so that lane group g
+// reads queries 4g..4g+3 and 16+4g..16+4g+3 as one 16-byte operand (positions 8g..8g+7).
+__device__ __forceinline__ int dkdv_tpos(int q) { return 8 * ((q >> 2) & 3) + 4 * (q >> 4) + (q & 3); }
+__device__ __forceinline__ void store_col16_dkdv(uint16_t* dst, uint4 v, int t) {
+  // thread t: row d = t/4, queries q0 = 8(t%4) .. q0+7, in two halves of four
+  const int d = t >> 2, q0 = (t & 3) * 8;
+  uint16_t* row = dst + d * BW_TROW;
+  *reinterpret_cast<uint2*>(row + dkdv_tpos(q0)) = make_uint2(v.x, v.y);
+  *reinterpret_cast<uint2*>(row + dkdv_tpos(q0 + 4)) = make_uint2(v.z, v.w);
+}
+
+// Workgroup: 8 waves (two per SIMD) = keys 128 kt .. 128 kt + 127 of (b, hk); wave w owns keys
+// 128 kt + 16 w + [0, 16), its K and V rows held in registers as B operands and its dK^T, dV^T
+// accumulators (128 x 16 each) in registers. Steps n = (query head, 32-query block), the blocks from
+// the last one down to 4kt: workgroups that run together read the same query block at the same time.
+// Per step, keys on the MFMA columns: S = Q K^T and dP = dO V^T (two 16-query row tiles, K = D in four
+// 32-wide steps), P and dS elementwise in the accumulators, then dV^T += dO^T P and dK^T += Q^T dS with
+// P and dS as the B operand straight from those accumulators (element i of row tile mt is query
+// 16mt + 4g + i: slot (g, e) of the contraction is query 16(e/4) + 4g + e%4, the order in which the
+// transposed tiles are stored). The next step's tiles are fetched into registers while the current
+// one computes, then stored into the other LDS buffer.
+constexpr int DKDV_NBUF = 3;  // LDS ring: the step computing, the next one (stored), the one after (arriving)
 struct DkdvTiles {
   uint16_t q[32 * BW_ROW], g[32 * BW_ROW], qt[128 * BW_TROW], gt[128 * BW_TROW];
   float l[32], d[32];
 };
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams P) {
-  __shared__ __align__(16) DkdvTiles buf[2];
-  const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(const BwdParams P) {
+  __shared__ __align__(16) DkdvTiles buf[DKDV_NBUF];
+  const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int G = P.Hq / P.Hkv;
-  const int kb = 4 * kt + wave, key0 = 32 * kb;
-  const bool valid = key0 < S;
+  const int key0 = 128 * kt + 16 * wave;
+  const bool valid = key0 < S;  // S % 32 == 0: a wave's 16 keys are all inside or all outside
   const int64_t bhk = (int64_t)b * P.Hkv + hk;
-  // This wave's K and V rows as B operands: lane (key c, h), step s holds columns 16s + 8h + [0, 8).
-  v8bf kop[8], vop[8];
-  const int krow = valid ? key0 + c : 0;
+  // B operands: lane (key n, g), step s holds columns 32s + 8g + [0, 8) of the key's K and V rows.
+  v8bf kop[4], vop[4];
+  const int krow = valid ? key0 + n : 0;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    kop[s] = ld8bf(P.kd + (bhk * S + krow) * 128 + 16 * s + 8 * h);
-    vop[s] = ld8bf(P.vd + (bhk * S + krow) * 128 + 16 * s + 8 * h);
+  for (int s = 0; s < 4; ++s) {
+    kop[s] = ld8bf(P.kd + (bhk * S + krow) * 128 + 32 * s + 8 * g);
+    vop[s] = ld8bf(P.vd + (bhk * S + krow) * 128 + 32 * s + 8 * g);
   }
-  v16f dkT[4], dvT[4];
+  v4f dkT[8], dvT[8];  // tile dt: lane (key n, g), element i <-> column d = 16dt + 4g + i
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
+    for (int i = 0; i < 4; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
   const int nqb = S / 32, qb0 = 4 * kt, per_head = nqb - qb0, nsteps = G * per_head;
-  uint4 rq0, rq1, rg0, rg1, rqt0, rqt1, rgt0, rgt1;
-  float rl = 0.f, rd = 0.f;
-  // step n: query head hk*G + n / per_head, query block nqb - 1 - n % per_head
-#define DKDV_FETCH(n)                                                           \
-  do {                                                                          \
-    const int hq_ = hk * G + (n) / per_head, q0_ = 32 * (nqb - 1 - (n) % per_head); \
-    const int64_t bhq_ = (int64_t)b * P.Hq + hq_;                               \
-    const uint16_t *q_ = P.qd + bhq_ * S * 128, *g_ = P.gd + bhq_ * S * 128;    \
-    const uint16_t *qt_ = P.qdt + bhq_ * 128 * S, *gt_ = P.gdt + bhq_ * 128 * S; \
-    rq0 = load_row16(q_, q0_, tid, 0);                                          \
-    rq1 = load_row16(q_, q0_, tid, 1);                                          \
-    rg0 = load_row16(g_, q0_, tid, 0);                                          \
-    rg1 = load_row16(g_, q0_, tid, 1);                                          \
-    rqt0 = load_col16(qt_, S, q0_, tid, 0);                                     \
-    rqt1 = load_col16(qt_, S, q0_, tid, 1);                                     \
-    rgt0 = load_col16(gt_, S, q0_, tid, 0);                                     \
-    rgt1 = load_col16(gt_, S, q0_, tid, 1);                                     \
-    if (tid < 32) {                                                             \
-      rl = P.lse[bhq_ * S + q0_ + tid] * 1.4426950408889634f;                   \
-      rd = P.delta[bhq_ * S + q0_ + tid];                                       \
-    }                                                                           \
+  // Staging: thread t moves one 16-byte piece of each of Q, dO (row t/16, columns 8(t%16)..), Q^T and
+  // dO^T (row d = t/4, queries 8(t%4)..), and threads 0..31 the lse and Delta of query t.
+  // Two register sets alternate: the tiles of step st + 2 are fetched during step st and stored at its
+  // end, so each fetch has two steps of time to arrive.
+  uint4 rq, rg, rqt, rgt, rq2, rg2, rqt2, rgt2;
+  float rl = 0.f, rd = 0.f, rl2 = 0.f, rd2 = 0.f;
+  const int rrow = tid >> 4, rcol = (tid & 15) * 8, tdd = tid >> 2, tq0 = (tid & 3) * 8;
+#define DKDV_FETCH(n_, RQ, RG, RQT, RGT, RL, RD)                                           \
+  do {                                                                                     \
+    const int hq_ = hk * G + (n_) / per_head, q0_ = 32 * (nqb - 1 - (n_) % per_head);      \
+    const int64_t bhq_ = (int64_t)b * P.Hq + hq_;                                          \
+    RQ = *reinterpret_cast<const uint4*>(P.qd + (bhq_ * S + q0_ + rrow) * 128 + rcol);     \
+    RG = *reinterpret_cast<const uint4*>(P.gd + (bhq_ * S + q0_ + rrow) * 128 + rcol);     \
+    RQT = *reinterpret_cast<const uint4*>(P.qdt + (bhq_ * 128 + tdd) * S + q0_ + tq0);     \
+    RGT = *reinterpret_cast<const uint4*>(P.gdt + (bhq_ * 128 + tdd) * S + q0_ + tq0);     \
+    if (tid < 32) {                                                                        \
+      RL = P.lse[bhq_ * S + q0_ + tid] * 1.4426950408889634f;                              \
+      RD = P.delta[bhq_ * S + q0_ + tid];                                                  \
+    }                                                                                      \
   } while (0)
-#define DKDV_PUT(t)                \
-  do {                             \
-    store_row16(t.q, rq0, tid, 0); \
-    store_row16(t.q, rq1, tid, 1); \
-    store_row16(t.g, rg0, tid, 0); \
-    store_row16(t.g, rg1, tid, 1); \
-    store_col16(t.qt, rqt0, tid, 0); \
-    store_col16(t.qt, rqt1, tid, 1); \
-    store_col16(t.gt, rgt0, tid, 0); \
-    store_col16(t.gt, rgt1, tid, 1); \
-    if (tid < 32) {                \
-      t.l[tid] = rl;               \
-      t.d[tid] = rd;               \
-    }                              \
+#define DKDV_PUT(t_, RQ, RG, RQT, RGT, RL, RD)                               \
+  do {                                                                       \
+    *reinterpret_cast<uint4*>((t_).q + rrow * BW_ROW + rcol) = RQ;           \
+    *reinterpret_cast<uint4*>((t_).g + rrow * BW_ROW + rcol) = RG;           \
+    store_col16_dkdv((t_).qt, RQT, tid);                                     \
+    store_col16_dkdv((t_).gt, RGT, tid);                                     \
+    if (tid < 32) {                                                          \
+      (t_).l[tid] = RL;                                                      \
+      (t_).d[tid] = RD;                                                      \
+    }                                                                        \
   } while (0)
-  DKDV_FETCH(0);
-  DKDV_PUT(buf[0]);
-  __syncthreads();
-  for (int n = 0; n < nsteps; ++n) {
-    if (n + 1 < nsteps) DKDV_FETCH(n + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    const DkdvTiles& T = buf[n & 1];
-    const int qb = nqb - 1 - n % per_head;
-    {  // every wave computes every step (branch-free: the accumulators stay in place); masked below
-      // S = Q K^T and dP = dO V^T: lane (key c, h), element i <-> query 8(i/4) + 4h + i%4 of the block
-      // All operand reads of a phase are issued before its MFMAs, so LDS latency is paid once.
-      v8bf qa[8], ga[8];
+  // One step's compute on the tiles in T (step st): S, dP, P, dS, and the dV^T, dK^T updates.
+  auto dkdv_compute = [&](const DkdvTiles& T, int st) {
+    const int qb = nqb - 1 - st % per_head;
+    {  // every wave computes every step (branch-free); key > query is masked below
+      v4f sacc[2], pacc[2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        qa[s] = ld8bf(T.q + c * BW_ROW + 16 * s + 8 * h);
-        ga[s] = ld8bf(T.g + c * BW_ROW + 16 * s + 8 * h);
-      }
-      v16f sacc, pacc;
+      for (int mt = 0; mt < 2; ++mt) {
+        v8bf qa[4], ga[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sacc = mfma_bf16(qa[s], kop[s], sacc);
-        pacc = mfma_bf16(ga[s], vop[s], pacc);
-      }
-      // A operands of the dV/dK products (row d = 32dt + c of the transposed tiles, slot order)
-      v8bf gta[2][4], qta[2][4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          gta[t][dt] = ld8bf(T.gt + (32 * dt + c) * BW_TROW + 16 * t + 8 * h);
-          qta[t][dt] = ld8bf(T.qt + (32 * dt + c) * BW_TROW + 16 * t + 8 * h);
+        for (int s = 0; s < 4; ++s) {
+          qa[s] = ld8bf(T.q + (16 * mt + n) * BW_ROW + 32 * s + 8 * g);
+          ga[s] = ld8bf(T.g + (16 * mt + n) * BW_ROW + 32 * s + 8 * g);
         }
-      float4 l4[4], d4[4];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        l4[g4] = *reinterpret_cast<const float4*>(T.l + 8 * g4 + 4 * h);
-        d4[g4] = *reinterpret_cast<const float4*>(T.d + 8 * g4 + 4 * h);
-      }
-      const int qoff = 32 * (qb - kb);  // query - key offset of the two blocks
+        for (int i = 0; i < 4; ++i) sacc[mt][i] = pacc[mt][i] = 0.f;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float lv[4] = {l4[g4].x, l4[g4].y, l4[g4].z, l4[g4].w};
-        const float dv[4] = {d4[g4].x, d4[g4].y, d4[g4].z, d4[g4].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e, qq = 8 * g4 + 4 * h + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lv[e]));
-          if (c > qoff + qq) p = 0.f;  // key after query (whole block when qb < kb)
-          sacc[i] = p;                       // P
-          pacc[i] = p * (pacc[i] - dv[e]);   // dS
+        for (int s = 0; s < 4; ++s) {
+          sacc[mt] = mfma16(qa[s], kop[s], sacc[mt]);
+          pacc[mt] = mfma16(ga[s], vop[s], pacc[mt]);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries, two 16-query steps. Step t, B slot
-      // (h, e) is accumulator element 8t + e: query 16t + 8(e/4) + 4h + e%4, the A operand's slot
-      // order in the transposed tile.
+      // P = 2^(S scale log2e - lse log2e) and dS = P (dP - Delta); query 16mt + 4g + i, key key0 + n
+      const int koff = key0 - 32 * qb;  // key - query offset of the two blocks' first tokens
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const v8bf pb = to_bf16(sacc, t), sb = to_bf16(pacc, t);
+      for (int mt = 0; mt < 2; ++mt) {
+        const float4 l4 = *reinterpret_cast<const float4*>(T.l + 16 * mt + 4 * g);
+        const float4 d4 = *reinterpret_cast<const float4*>(T.d + 16 * mt + 4 * g);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          dvT[dt] = mfma_bf16(gta[t][dt], pb, dvT[dt]);
-          dkT[dt] = mfma_bf16(qta[t][dt], sb, dkT[dt]);
+        for (int i = 0; i < 4; ++i) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], P.scale_log2, -lv[i]));
+          if (n + koff > 16 * mt + 4 * g + i) p = 0.f;  // key after query
+          sacc[mt][i] = p;
+          pacc[mt][i] = p * (pacc[mt][i] - dv[i]);
         }
+      }
+      v8bf pb, sb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[e] = (__bf16)sacc[e >> 2][e & 3];
+        sb[e] = (__bf16)pacc[e >> 2][e & 3];
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: one MFMA per 16-row tile of D (K = the 32 queries)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v8bf gta = ld8bf(T.gt + (16 * dt + n) * BW_TROW + 8 * g);
+        const v8bf qta = ld8bf(T.qt + (16 * dt + n) * BW_TROW + 8 * g);
+        dvT[dt] = mfma16(gta, pb, dvT[dt]);
+        dkT[dt] = mfma16(qta, sb, dkT[dt]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (n + 1 < nsteps) DKDV_PUT(buf[(n + 1) & 1]);
-    // Unconditional vmcnt(0): the prefetch registers are free on every path out of the step.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+  };
+  DKDV_FETCH(0, rq, rg, rqt, rgt, rl, rd);
+  DKDV_PUT(buf[0], rq, rg, rqt, rgt, rl, rd);
+  if (nsteps > 1) DKDV_FETCH(1, rq, rg, rqt, rgt, rl, rd);  // set A: step 1, stored at the end of step 0
+  __syncthreads();
+  // Step st computes from slot st % 3. During it the tiles of step st + 2 are fetched into the register
+  // set that does not hold step st + 1; at its end step st + 1's tiles are stored into slot (st + 1) % 3,
+  // last read by step st - 2, two barriers earlier. The loop is unrolled by two so that the two
+  // register sets keep fixed roles.
+#define DKDV_STEP(st, FQ, FG, FQT, FGT, FL, FD, PQ, PG, PQT, PGT, PL, PD) \
+  do {                                                                   \
+    if ((st) + 2 < nsteps) DKDV_FETCH((st) + 2, FQ, FG, FQT, FGT, FL, FD); \
+    __builtin_amdgcn_sched_barrier(0);                                   \
+    dkdv_compute(buf[(st) % DKDV_NBUF], (st));                           \
+    __builtin_amdgcn_sched_barrier(0);                                   \
+    if ((st) + 1 < nsteps) DKDV_PUT(buf[((st) + 1) % DKDV_NBUF], PQ, PG, PQT, PGT, PL, PD); \
+    __syncthreads();                                                     \
+  } while (0)
+  for (int st = 0; st < nsteps; st += 2) {
+    DKDV_STEP(st, rq2, rg2, rqt2, rgt2, rl2, rd2, rq, rg, rqt, rgt, rl, rd);
+    if (st + 1 < nsteps) DKDV_STEP(st + 1, rq, rg, rqt, rgt, rl, rd, rq2, rg2, rqt2, rgt2, rl2, rd2);
   }
+#undef DKDV_STEP
 #undef DKDV_FETCH
 #undef DKDV_PUT
   if (!valid) return;
-  // lane (key c, h), element i of tile dt: column 32dt + 8(i/4) + 4h + i%4
-  const int64_t off = b * P.ksb + (int64_t)(key0 + c) * P.kss + hk * P.ksh + 4 * h;
+  // lane (key n, g), element i of tile dt: column 16dt + 4g + i
+  const int64_t off = b * P.ksb + (int64_t)(key0 + n) * P.kss + hk * P.ksh + 4 * g;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int64_t o = off + 32 * dt + 8 * g4;
-      uint2 pk, pv;
-      pk.x = f32_to_bf16(dkT[dt][4 * g4] * P.scale) | (f32_to_bf16(dkT[dt][4 * g4 + 1] * P.scale) << 16);
-      pk.y = f32_to_bf16(dkT[dt][4 * g4 + 2] * P.scale) | (f32_to_bf16(dkT[dt][4 * g4 + 3] * P.scale) << 16);
-      pv.x = f32_to_bf16(dvT[dt][4 * g4]) | (f32_to_bf16(dvT[dt][4 * g4 + 1]) << 16);
-      pv.y = f32_to_bf16(dvT[dt][4 * g4 + 2]) | (f32_to_bf16(dvT[dt][4 * g4 + 3]) << 16);
-      *reinterpret_cast<uint2*>(P.dk + o) = pk;
-      *reinterpret_cast<uint2*>(P.dv + o) = pv;
-    }
+  for (int dt = 0; dt < 8; ++dt) {
+    uint2 pk, pv;
+    pk.x = f32_to_bf16(dkT[dt][0] * P.scale) | (f32_to_bf16(dkT[dt][1] * P.scale) << 16);
+    pk.y = f32_to_bf16(dkT[dt][2] * P.scale) | (f32_to_bf16(dkT[dt][3] * P.scale) << 16);
+    pv.x = f32_to_bf16(dvT[dt][0]) | (f32_to_bf16(dvT[dt][1]) << 16);
+    pv.y = f32_to_bf16(dvT[dt][2]) | (f32_to_bf16(dvT[dt][3]) << 16);
+    *reinterpret_cast<uint2*>(P.dk + off + 16 * dt) = pk;
+    *reinterpret_cast<uint2*>(P.dv + off + 16 * dt) = pv;
+  }
 }
 
 // ---- dQ ----------------------------------------------------------------------------------------
@@ -467,7 +482,7 @@ hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* 
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.qsb = qsb; p.qss = qss; p.qsh = qsh; p.ksb = ksb; p.kss = kss; p.ksh = ksh;
   const unsigned tiles = (unsigned)((S + 127) / 128);
-  bwd_dkdv_kernel<<<dim3(tiles, (unsigned)Hkv, (unsigned)B), 256, 0, stream>>>(p);
+  bwd_dkdv_kernel<<<dim3(tiles, (unsigned)Hkv, (unsigned)B), 512, 0, stream>>>(p);
   bwd_dq_kernel<<<dim3(tiles, (unsigned)Hq, (unsigned)B), 256, 0, stream>>>(p);
   return hipGetLastError();
 }
