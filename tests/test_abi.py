@@ -118,3 +118,55 @@ def test_leaky_validation(args, status, needle):
                                                 a["Hkv"], a["D"], 0.1, FAKE, S * Hq * 128, Hq * 128, a["osh"],
                                                 a["dtype"], None, None))
     assert st == status and needle in msg, (st, msg)
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(D=64), 3, "D = 64"),
+    (dict(S=80), 2, "multiple of 32"),
+    (dict(Hq=3, Hkv=2), 2, "multiple of Hkv"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(dout=FAKE + 8), 4, "dout is not 16-byte aligned"),
+    (dict(ksh=100), 4, "multiples of 8"),
+    (dict(qss=64), 2, "overlap"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(ws=FAKE + 16), 4, "256-byte aligned"),
+    (dict(ws_short=True), 3, "workspace"),
+])
+def test_backward_validation(args, status, needle):
+    """mxfa_attn_bwd refuses bad shapes, pointers, views and workspaces before any device work."""
+    a = dict(B=1, S=64, Hq=4, Hkv=2, D=128, lse=FAKE, dout=FAKE, ws=FAKE, ws_short=False, ksh=128, qss=512)
+    a.update(args)
+    L = mx.lib()
+    S, Hq, Hkv = a["S"], a["Hq"], a["Hkv"]
+    need = L.mxfa_attn_bwd_workspace_bytes(a["B"], S, Hq, Hkv, 128) if a["D"] == 128 else 1 << 20
+    assert need > 0
+    st, msg = _err(L.mxfa_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["lse"], a["dout"], a["B"], S, Hq, Hkv,
+                                   a["D"], 0.1, S * Hq * 128, a["qss"], 128, S * Hkv * 128, Hkv * 128, a["ksh"],
+                                   a["ws"], need - 1 if a["ws_short"] else need, FAKE, FAKE, FAKE, None))
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_backward_workspace_grows_with_the_problem():
+    L = mx.lib()
+    small = L.mxfa_attn_bwd_workspace_bytes(1, 64, 4, 2, 128)
+    assert small > 0
+    assert L.mxfa_attn_bwd_workspace_bytes(1, 128, 4, 2, 128) > small
+    assert L.mxfa_attn_bwd_workspace_bytes(2, 64, 4, 2, 128) > small
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(D=32), 3, "D = 32"),
+    (dict(vt=None), 1, "vt is NULL"),
+    (dict(oss=136), 4, "multiples of 16"),
+    (dict(o=FAKE + 4), 4, "o_codes is not 16-byte aligned"),
+    (dict(lse=FAKE + 4), 4, "lse_out is not 16-byte aligned"),
+])
+def test_fused_mxfp8_validation(args, status, needle):
+    """The MXFP8-output forward needs 16-element strides (16-byte code rows) and checks them first."""
+    a = dict(D=128, vt=FAKE, oss=4 * 128, o=FAKE, lse=FAKE)
+    a.update(args)
+    S, Hq = 64, 4
+    st, msg = _err(mx.lib().mxfa_attn_fwd_fused_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["vt"], FAKE, 1, S, Hq, 2,
+                                                      a["D"], 0.1, a["o"], S * Hq * 128, a["oss"], 128, FAKE,
+                                                      a["lse"], None))
+    assert st == status and needle in msg, (st, msg)
