@@ -25,11 +25,14 @@
 //    codes; the normaliser sums p / 2^k per block and rescales the two block sums by 2^k. P.V is
 //    the block-scaled FP8 MFMA again, on the columnwise V codes (keys contiguous per column).
 //  * O^T leaves one query per lane too, so the rescale and the final 1/l are per-lane scalars.
-//  * K and V tiles of 64 keys are staged in LDS once per workgroup and shared by the 4 waves; the
-//    LDS is double-buffered and the next tile's global loads are in flight while the current tile
-//    computes, one barrier per tile.
-//  * Two workgroups per CU (two waves per SIMD, 212 VGPRs each): the softmax VALU work of one wave
-//    overlaps the MFMAs and memory waits of the other.
+//  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the LDS flag), once per
+//    workgroup, shared by the 4 waves: a ring of three tiles, one barrier per tile. No register holds
+//    a tile in flight.
+//  * Software pipeline: while a wave runs the softmax of tile n, it issues the four score MFMAs of
+//    tile n + 1, one per group of exponentials, so the matrix core works beside the VALU within the
+//    wave; tile n + 2 arrives meanwhile. The ordinary causal variant keeps a plain loop.
+//  * Two workgroups per CU (two waves per SIMD, up to 254 VGPRs each): the softmax VALU work of one
+//    wave also overlaps the MFMAs and memory waits of the other.
 //  * Full tiles and the half tile at the end of a wave's range are separate code paths, so the
 //    common path has no per-element select.
 //  * One-dimensional grid in global longest-first order: all (batch, head) pairs of the last query
@@ -44,8 +47,12 @@ namespace mxfa {
 
 constexpr int CB_BM = 128;    // queries per workgroup (4 waves x 32)
 constexpr int CB_BN = 64;     // keys per tile (two 32-key MX blocks)
-constexpr int CB_KROW = 144;  // LDS bytes per K row (128 codes + 16 pad: conflict-free 16-byte reads)
-constexpr int CB_VROW = 80;   // LDS bytes per V column (64 codes + 16 pad)
+// K and V tiles go from HBM straight into LDS (buffer loads with the LDS flag: each lane's 16 bytes
+// land at consecutive LDS addresses), so their rows are unpadded. Reads stay conflict-free through an
+// XOR swizzle of the 16-byte chunks: chunk x of K row r sits in slot x ^ ((r >> 1) & 7), chunk x of V
+// column d in slot x ^ ((d >> 2) & 3).
+constexpr int CB_KROW = 128;  // LDS bytes per K row
+constexpr int CB_VROW = 64;   // LDS bytes per V column (keys contiguous)
 constexpr float CB_PMAX_LAZY = 256.0f;  // raise T once a block maximum of p exceeds 2^8
 constexpr int CB_RSRC_W3 = 0x00020000;  // buffer descriptor word 3 on gfx9: 32-bit data, raw offsets
 
@@ -109,28 +116,32 @@ __device__ __forceinline__ void swap32f(float& x, float& y) {
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-#define TILE_LOAD(k0, k1, v0, v1, sc, kt0)                                           \
-  do {                                                                               \
-    k0 = bload16(rk, kvoff, (kt0) * 128);                                            \
-    k1 = bload16(rk, kvoff + 16, (kt0) * 128);                                       \
-    v0 = bload16(rv, vvoff, (kt0));                                                  \
-    v1 = bload16(rv, vvoff + 16, (kt0));                                             \
-    if (wave_u < 2)                                                                  \
+// Thread tid fills LDS chunks c = 256 i + tid (i = 0, 1) of the K tile (row c/8, slot c%8) and of the
+// V tile (column c/4, slot c%4); the wave's 64 chunks of one instruction are contiguous.
+#define TILE_LOAD(T, sc, kt0)                                                                    \
+  do {                                                                                           \
+    bload_lds16(rk, (T).k + 16 * (64 * wave_u), kvoff0, (kt0) * 128);                            \
+    bload_lds16(rk, (T).k + 16 * (256 + 64 * wave_u), kvoff1, (kt0) * 128);                      \
+    bload_lds16(rv, (T).v + 16 * (64 * wave_u), vvoff0, (kt0));                                  \
+    bload_lds16(rv, (T).v + 16 * (256 + 64 * wave_u), vvoff1, (kt0));                            \
+    if (wave_u < 2)                                                                              \
       sc = __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, wave_u == 0 ? (kt0) * 4 : ((kt0) >> 5) * 128, 0); \
   } while (0)
 
 __device__ __forceinline__ int k_lds_row(int kk) {
   return (kk & 32) | (((kk >> 2) & 3) << 3) | (((kk >> 4) & 1) << 2) | (kk & 3);
 }
+__device__ __forceinline__ int k_row_key(int r) {  // inverse of k_lds_row: the key stored in LDS row r
+  return (r & 32) | (((r >> 3) & 3) << 2) | (((r >> 2) & 1) << 4) | (r & 3);
+}
+__device__ __forceinline__ int k_slot(int r, int x) { return x ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int v_slot(int d, int x) { return x ^ ((d >> 2) & 3); }
+// 16 bytes per lane from a buffer resource straight into LDS: lane l's bytes go to lds + 16 l.
+__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
 
-__device__ __forceinline__ void store_tile(TileSmem& t, uint4 k0, uint4 k1, uint4 v0, uint4 v1, uint32_t sc,
-                                           int tid) {
-  const int kr = k_lds_row(tid >> 2), kch = (tid & 3) * 32;
-  *reinterpret_cast<uint4*>(t.k + kr * CB_KROW + kch) = k0;
-  *reinterpret_cast<uint4*>(t.k + kr * CB_KROW + kch + 16) = k1;
-  const int d = tid >> 1, hv = (tid & 1) * 32;
-  *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv) = v0;
-  *reinterpret_cast<uint4*>(t.v + d * CB_VROW + hv + 16) = v1;
+__device__ __forceinline__ void store_scales(TileSmem& t, uint32_t sc, int tid) {
   if (tid < 64) {
     // bytes s0 s2 s1 s3: the 16-bit half hf then holds the scales of D-blocks hf and 2 + hf
     t.ks[k_lds_row(tid)] = __builtin_amdgcn_perm(sc, sc, 0x03010200u);
@@ -166,11 +177,12 @@ __device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const
   int ksc[nkt];
 #pragma unroll
   for (int kt = 0; kt < nkt; ++kt) {
-    const uint8_t* kr = t.k + (32 * kt + c) * CB_KROW + 16 * hf;
+    const int r = 32 * kt + c;
+    const uint8_t* kr = t.k + r * CB_KROW;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
-      kop[kt][m] = make_v8i(*reinterpret_cast<const uint4*>(kr + 64 * m),
-                            *reinterpret_cast<const uint4*>(kr + 64 * m + 32));
+      kop[kt][m] = make_v8i(*reinterpret_cast<const uint4*>(kr + 16 * k_slot(r, 4 * m + hf)),
+                            *reinterpret_cast<const uint4*>(kr + 16 * k_slot(r, 4 * m + 2 + hf)));
     ksc[kt] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(t.ks) + (32 * kt + c) * 4 + 2 * hf);
   }
 #pragma unroll
@@ -184,48 +196,75 @@ __device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const
   for (int kt = 0; kt < nkt; ++kt) sacc[kt] = mfma_mx<1, 0>(kop[kt][1], qop[1], sacc[kt], ksc[kt], qsc[1]);
 }
 
-// Softmax, P quantisation and O^T += V^T P^T for one tile whose scores are in sacc. kFull: both
-// 32-key blocks are visible keys of this wave; otherwise only the first one is (the second one's p
-// is zero). kMaskBlk (ordinary causal variant only): that block is the wave's own 32-token block, of
-// which query qw + c sees keys qw .. qw + c; the others get p = 0, and its E8M0 comes from the
-// visible keys.
-template <bool kFull, int kMaskBlk = -1>
-__device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const TileSmem& t, float scale_log2,
-                                           int c, int hf, bool first) {
+// Softmax, P quantisation and O^T += V^T P^T for one tile whose scores are in sacc, with the score
+// MFMAs of the next tile (in tn, into snext) interleaved. kFull: both 32-key blocks are visible keys of
+// this wave; otherwise only the first one is (the second one's p is zero). kNext: the next tile's
+// scores to compute, 2 both of its blocks, 1 its first block, 0 none. They depend on nothing this
+// softmax computes, so the matrix core works on them while this wave's VALU runs the softmax: one
+// MFMA per group of exponentials. kMaskBlk (ordinary causal variant only, with kNext = 0): that block
+// is the wave's own 32-token block, of which query qw + c sees keys qw .. qw + c; the others get
+// p = 0, and its E8M0 comes from the visible keys.
+template <bool kFull, int kNext = 0, int kMaskBlk = -1>
+__device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const TileSmem& t, v16f (&snext)[2],
+                                           const TileSmem& tn, const v8i (&qop)[2], const int (&qsc)[2],
+                                           float scale_log2, int c, int hf, bool first) {
+  static_assert(kMaskBlk < 0 || kNext == 0, "the masked own block is the wave's last tile");
+  constexpr int nmf = 2 * kNext;  // score MFMAs of the next tile: (kt, m) = (0,0), (1,0), (0,1), (1,1)
   // Lane (c, hf), element i of block kt holds key 32kt + 16hf + i of the tile, query c.
   if (kMaskBlk >= 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (16 * hf + i > c) sacc[kMaskBlk][i] = -INFINITY;
   }
-
-  // The V^T operands of this tile's P.V are read from LDS first, so their latency hides under the
-  // softmax below. Lane (c, hf), tile dt: column 32dt + c, keys 16hf + [0,16) and 32 + 16hf + [0,16).
-  v8i vop[4];
+  // Next tile's K operand of MFMA j, read one group before it is used.
+  auto kread = [&](int j) {
+    const int kt = kNext == 2 ? (j & 1) : 0, m = kNext == 2 ? (j >> 1) : j;
+    const int r = 32 * kt + c;
+    const uint8_t* kr = tn.k + r * CB_KROW;
+    return make_v8i(*reinterpret_cast<const uint4*>(kr + 16 * k_slot(r, 4 * m + hf)),
+                    *reinterpret_cast<const uint4*>(kr + 16 * k_slot(r, 4 * m + 2 + hf)));
+  };
+  int ksc[2];
+  if (nmf > 0) {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const uint8_t* vr = t.v + (32 * dt + c) * CB_VROW + 16 * hf;
-    vop[dt] = make_v8i(*reinterpret_cast<const uint4*>(vr), *reinterpret_cast<const uint4*>(vr + 32));
+    for (int kt = 0; kt < kNext; ++kt)
+      ksc[kt] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(tn.ks) + (32 * kt + c) * 4 + 2 * hf);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) snext[kt][i] = 0.f;
   }
-  const uint32_t vsw = *reinterpret_cast<const uint32_t*>(t.vs + hf * 128 + c * 4);
-  __builtin_amdgcn_sched_barrier(0);
+  v8i kcur = nmf > 0 ? kread(0) : v8i{};
+  // This tile's V^T operands: lane (c, hf), tile dt: column 32dt + c, keys 16hf + [0,16) and
+  // 32 + 16hf + [0,16). Read here when no next-tile scores are due (their latency hides under the
+  // softmax), else in the last group, once the K operands are consumed (register pressure).
+  v8i vop[4];
+  uint32_t vsw;
+  auto vread = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int d = 32 * dt + c;
+      const uint8_t* vr = t.v + d * CB_VROW;
+      vop[dt] = make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
+                         *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
+    }
+    vsw = *reinterpret_cast<const uint32_t*>(t.vs + hf * 128 + c * 4);
+  };
+  if (nmf == 0) vread();
 
-  // ---- block maxima of the raw scores, the lazy exponent, the E8M0 of each P block ------------
   float m0 = sacc[0][0], m1 = kFull ? sacc[1][0] : -INFINITY;
 #pragma unroll
   for (int i = 1; i < 16; ++i) {
     m0 = vmax(m0, sacc[0][i]);
     if (kFull) m1 = vmax(m1, sacc[1][i]);
   }
-  swap32f(m0, m1);  // lanes 0..31 now see both halves of block 0, lanes 32..63 of block 1
+  swap32f(m0, m1);
   float M0 = vmax(m0, m1), M1 = M0;
-  swap32f(M0, M1);  // every lane: M0 = block-0 maximum, M1 = block-1 maximum (raw scores)
+  swap32f(M0, M1);
   float negT = -st.T;
   float pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
   float pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
   if (first || __any(vmax(pm0, pm1) > CB_PMAX_LAZY)) {
-    // Set T on a wave's first tile, and afterwards raise it when a block maximum of p would exceed
-    // 2^8: T += ceil(max (t - T)), rescaling O and l by the exact power of two 2^-shift.
     const float shift = ceilf(fmaf(kFull ? vmax(M0, M1) : M0, scale_log2, negT));
     const float f = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
@@ -238,22 +277,23 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
     pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
   }
-  // E8M0 byte 127 + k of each P block: k = E - 8, plus 1 when the mantissa of the block maximum
-  // exceeds 1.75 (adding 2^21 - 1 to the bits carries into the exponent exactly then). Exponent
-  // -127 (byte 0) is only reached by blocks whose largest p is below 2^-118; they use byte 1, as the
-  // scale byte of the P operand must not be 0.
   const int e0 = max((int)((f2u(pm0) + 0x1FFFFFu) >> 23), 9) - 8;
   const int e1 = kFull ? max((int)((f2u(pm1) + 0x1FFFFFu) >> 23), 9) - 8 : 1;
   const float t127 = 127.f - st.T;
-  const float nb0 = t127 - (float)e0, nb1 = t127 - (float)e1;  // -T - k of each block
+  const float nb0 = t127 - (float)e0, nb1 = t127 - (float)e1;
 
-  // ---- p / 2^k = 2^(t - T - k), its block sums and its E4M3 codes, four at a time ---------------
-  // Codes go straight into the B operand: lane (c, hf) bytes 4g..4g+3 are keys 16hf + 4g + [0,4) of
-  // block 0 and bytes 16 + 4g.. the same keys of block 1.
   v8i pop;
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
+    v8i knext{};
+    if (g < nmf) {
+      const int kt = kNext == 2 ? (g & 1) : 0, m = kNext == 2 ? (g >> 1) : g;
+      snext[kt] = m == 0 ? mfma_mx<0, 0>(kcur, qop[0], snext[kt], ksc[kt], qsc[0])
+                         : mfma_mx<1, 0>(kcur, qop[1], snext[kt], ksc[kt], qsc[1]);
+      if (g + 1 < nmf) knext = kread(g + 1);
+    }
+    if (nmf > 0 && g == 3) vread();
     float q[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[0][4 * g + e], scale_log2, nb0));
@@ -267,11 +307,17 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     } else {
       pop[4 + g] = 0;
     }
+    if (g + 1 < nmf) {
+      // order: this group's codes are complete here, and the next MFMA's operand is used only after
+      int a = pop[g], b2 = pop[4 + g];
+      asm("" : "+v"(a), "+v"(b2), "+v"(knext));
+      pop[g] = a;
+      pop[4 + g] = b2;
+      kcur = knext;
+    }
   }
   st.lsum += kFull ? ldexpf(ls0, e0 - 127) + ldexpf(ls1, e1 - 127) : ldexpf(ls0, e0 - 127);
   const int psc = hf ? e1 : e0;
-
-  // ---- O^T += V^T P^T over the four 32-column tiles of D (V scale: byte dt of vsw) ------------
   st.o[0] = mfma_mx<0, 0>(vop[0], pop, st.o[0], (int)vsw, psc);
   st.o[1] = mfma_mx<1, 0>(vop[1], pop, st.o[1], (int)vsw, psc);
   st.o[2] = mfma_mx<2, 0>(vop[2], pop, st.o[2], (int)vsw, psc);
@@ -297,7 +343,8 @@ struct AttnParams {
 // LDS: the double-buffered K/V tiles of the main loop, reused afterwards (fused epilogue) for each
 // wave's decoded token-normalised own-block V, 32 keys x 128 columns of bf16 (exact: E4M3 values times
 // a power of two need 4 significant bits).
-constexpr int CB_LDS_BYTES = 2 * sizeof(TileSmem);
+constexpr int CB_NBUF = 3;  // ring: the tile being finished, the next one (its scores), the one arriving
+constexpr int CB_LDS_BYTES = CB_NBUF * sizeof(TileSmem);
 static_assert(4 * 32 * 128 * 2 <= CB_LDS_BYTES, "the own-block V must fit the tile buffers");
 
 // kMode: MODE_COMPLETED, the completed-block partial (O_c, lse_c); MODE_FUSED, the whole attention of
@@ -344,8 +391,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   const __amdgpu_buffer_rsrc_t rs =
       wave_u == 0 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ks + bhk * S * 4), 0, S * 4, CB_RSRC_W3)
                 : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vcs + bhk * S * 4), 0, S * 4, CB_RSRC_W3);
-  const int kvoff = (tid >> 2) * 128 + (tid & 3) * 32, vvoff = (tid >> 1) * S + (tid & 1) * 32,
-            svoff = (tid & 63) * 4;
+  // Per-lane source offsets of the tile loads (the tile's own offset is a scalar): LDS chunk c of K is
+  // row r = c/8 (key k_row_key(r)), slot c%8, holding chunk k_slot(r, c%8); of V, column c/4, slot c%4.
+  int kvoff0, kvoff1, vvoff0, vvoff1;
+  {
+    const int c0 = tid, c1 = tid + 256;
+    kvoff0 = k_row_key(c0 >> 3) * 128 + 16 * k_slot(c0 >> 3, c0 & 7);
+    kvoff1 = k_row_key(c1 >> 3) * 128 + 16 * k_slot(c1 >> 3, c1 & 7);
+    vvoff0 = (c0 >> 2) * S + 16 * v_slot(c0 >> 2, c0 & 3);
+    vvoff1 = (c1 >> 2) * S + 16 * v_slot(c1 >> 2, c1 & 3);
+  }
+  const int svoff = (tid & 63) * 4;
 
   // Q^T operand (B of S^T = K Q^T) for the two 64-wide K steps over D. Lane (c, hf) holds bytes
   // d = 64m + 16hf + [0,16) and 64m + 32 + 16hf + [0,16) of query qw + c; its scale is that of
@@ -377,39 +433,80 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
 
   // Tile it of the workgroup's key range is full for this wave when 64(it+1) <= e_w, half (first
   // 32-key block only) when 64it < e_w < 64(it+1), and outside the wave's range when 64it >= e_w.
-  uint4 pk0, pk1, pv0, pv1;
   uint32_t psc = 0;
   if (ntiles > 0) {
-    TILE_LOAD(pk0, pk1, pv0, pv1, psc, 0);
-    store_tile(sm[0], pk0, pk1, pv0, pv1, psc, tid);
+    TILE_LOAD(sm[0], psc, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    store_scales(sm[0], psc, tid);
+  }
+  if (!kLeaky && ntiles > 1) {
+    TILE_LOAD(sm[1], psc, CB_BN);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    store_scales(sm[1], psc, tid);
   }
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  if (!kLeaky) {
+    // Software pipeline: iteration it runs the softmax and P.V of tile it on scores computed one
+    // iteration earlier, with the next tile's score MFMAs interleaved. Tile it lives in ring slot
+    // it % 3; tile it + 2 is loaded during iteration it straight into the slot of tile it - 1, which
+    // no wave reads after the barrier that ended iteration it - 1.
+    const int nfull = e_w / CB_BN;                   // full tiles of this wave
+    const int nt_w = nfull + (e_w % CB_BN ? 1 : 0);  // tiles with completed keys of this wave
+    v16f sa[2], sb[2];
+    if (nt_w > 0) {
+      if (nfull > 0)
+        scores<true>(sa, sm[0], qop, qsc, c, hf);
+      else
+        scores<false>(sa, sm[0], qop, qsc, c, hf);
+    }
+    auto step = [&](int it, v16f(&sc)[2], v16f(&sn)[2]) {
+      const int kt0 = it * CB_BN;
+      const int slot = it % CB_NBUF;
+      const int slot2 = slot == 0 ? CB_NBUF - 1 : slot - 1;  // (it + 2) % 3
+      if (it + 2 < ntiles) TILE_LOAD(sm[slot2], psc, kt0 + 2 * CB_BN);
+      const TileSmem& cur = sm[slot];
+      const TileSmem& nxt = sm[slot == CB_NBUF - 1 ? 0 : slot + 1];
+      if (it < nfull) {
+        if (it + 1 < nfull)
+          softmax_pv<true, 2>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+        else if (it + 1 < nt_w)
+          softmax_pv<true, 1>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+        else
+          softmax_pv<true, 0>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+      } else if (it < nt_w) {
+        softmax_pv<false, 0>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      if (it + 2 < ntiles) store_scales(sm[slot2], psc, tid);
+      __syncthreads();
+    };
+    // unrolled by two so that the two score buffers swap roles without register copies
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, sa, sb);
+      if (it + 1 < ntiles) step(it + 1, sb, sa);
+    }
+  }
+  // Ordinary causal variant: the plain loop (no next-tile scores), the own block masked per element.
+  for (int it = 0; kLeaky && it < ntiles; ++it) {
     const int kt0 = it * CB_BN;
-    // Prefetch the next tile (the last iteration fetches its own tile again; it is not stored).
-    const int kn = (it + 1 < ntiles) ? kt0 + CB_BN : kt0;
-    TILE_LOAD(pk0, pk1, pv0, pv1, psc, kn);
+    // Prefetch the next tile straight into the other buffer (not read in this iteration).
+    if (it + 1 < ntiles) TILE_LOAD(sm[(it + 1) & 1], psc, kt0 + CB_BN);
     const TileSmem& cur = sm[it & 1];
-    v16f sacc[2];
+    v16f sacc[2], none[2];
     if (kt0 + CB_BN <= e_w) {
       scores<true>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<true>(st, sacc, cur, scale_log2, c, hf, it == 0);
-    } else if (kt0 < e_w) {
-      scores<kLeaky>(sacc, cur, qop, qsc, c, hf);
-      if (kLeaky)  // completed block, then the own block (masked)
-        softmax_pv<true, 1>(st, sacc, cur, scale_log2, c, hf, it == 0);
-      else
-        softmax_pv<false>(st, sacc, cur, scale_log2, c, hf, it == 0);
-    } else if (kLeaky && wave_valid && kt0 == e_w) {  // the own block opens this tile (masked)
+      softmax_pv<true>(st, sacc, cur, none, cur, qop, qsc, scale_log2, c, hf, it == 0);
+    } else if (kt0 < e_w) {  // completed block, then the own block (masked)
+      scores<true>(sacc, cur, qop, qsc, c, hf);
+      softmax_pv<true, 0, 1>(st, sacc, cur, none, cur, qop, qsc, scale_log2, c, hf, it == 0);
+    } else if (wave_valid && kt0 == e_w) {  // the own block opens this tile (masked)
       scores<false>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<false, 0>(st, sacc, cur, scale_log2, c, hf, it == 0);
+      softmax_pv<false, 0, 0>(st, sacc, cur, none, cur, qop, qsc, scale_log2, c, hf, it == 0);
     }
-    if (it + 1 < ntiles) store_tile(sm[(it + 1) & 1], pk0, pk1, pv0, pv1, psc, tid);
-    // Unconditional vmcnt(0): the prefetch is complete on every path out of the iteration (the
-    // store above already needs it except on the last one). Without it the compiler must assume the
-    // prefetch registers may still be in flight at the top of the next iteration, and makes the
-    // first score MFMA wait for the new tile's loads, exposing their latency on every tile.
+    // The next tile's loads (LDS and scale word) are complete here on every path; then its scales
+    // are stored and the barrier publishes the tile.
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (it + 1 < ntiles) store_scales(sm[(it + 1) & 1], psc, tid);
     __syncthreads();
   }
 
