@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.mxfa_attn_fwd_fused.restype = I
         L.mxfa_attn_fwd_fused_mxfp8.argtypes = [P] * 8 + [I, I, I, I, I, F, P, I64, I64, I64, P, P, P]
         L.mxfa_attn_fwd_fused_mxfp8.restype = I
+        L.mxfa_attn_fwd_fused_bf16q.argtypes = [P, I64, I64, I64] + [P] * 6 + [I, I, I, I, I, F, P, I64, I64, I64, I,
+                                                                         P, P]
+        L.mxfa_attn_fwd_fused_bf16q.restype = I
         L.mxfa_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
         L.mxfa_attn_bwd_workspace_bytes.restype = SZ
         L.mxfa_attn_bwd.argtypes = six + [P, P, P, I, I, I, I, I, F, I64, I64, I64, I64, I64, I64, P, SZ, P, P, P, P]
@@ -192,6 +195,25 @@ def attn_fwd_fused(qc, qs, kc, ks, vc, vcs, vt, vta, softmax_scale: float | None
     _, _, _, _, osb, oss, osh = view_of(out, layout)
     _check(lib().mxfa_attn_fwd_fused(_p(qc), _p(qs), _p(kc), _p(ks), _p(vc), _p(vcs), _p(vt), _p(vta), B, S, Hq, Hkv,
                                      D, scale, _p(out), osb, oss, osh, _out_code(out.dtype), _p(lse), _stream(qc)))
+    return out, lse
+
+
+def attn_fwd_fused_bf16q(q, kc, ks, vc, vcs, vt, vta, softmax_scale: float | None = None, out_dtype=torch.bfloat16,
+                         layout: str = "bshd", out=None, lse=None):
+    """The fused forward with Q as bf16 (``layout`` view), quantised inside the attention kernel:
+    (out in ``layout``, lse [B,Hq,S]); equal to mxfp8_quantize(q) followed by attn_fwd_fused."""
+    B, S, Hq, D, qsb, qss, qsh = view_of(q, layout)
+    Hkv = kc.shape[1]
+    scale = default_scale(D) if softmax_scale is None else softmax_scale
+    if out is None:
+        shape = (B, S, Hq, D) if layout == "bshd" else (S, B, Hq, D)
+        out = torch.empty(shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _, _, _, _, osb, oss, osh = view_of(out, layout)
+    _check(lib().mxfa_attn_fwd_fused_bf16q(_p(q), qsb, qss, qsh, _p(kc), _p(ks), _p(vc), _p(vcs), _p(vt), _p(vta), B,
+                                           S, Hq, Hkv, D, scale, _p(out), osb, oss, osh, _out_code(out.dtype),
+                                           _p(lse), _stream(q)))
     return out, lse
 
 

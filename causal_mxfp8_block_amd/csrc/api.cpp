@@ -101,22 +101,21 @@ int hip_status(hipError_t e, const char* what) {
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// attn_fwd's workspace: the K and V encodings (Q is quantised inside the attention kernel).
 struct Workspace {
-  uint8_t *qc, *qs, *kc, *ks, *vc, *vcs, *vt, *vta;
+  uint8_t *kc, *ks, *vc, *vcs, *vt, *vta;
   size_t bytes;
 };
 
 Workspace carve(void* base, int B, int S, int Hq, int Hkv) {
   Workspace w{};
-  const size_t nq = (size_t)B * Hq * S, nk = (size_t)B * Hkv * S;
+  const size_t nk = (size_t)B * Hkv * S;
   size_t off = 0;
   auto take = [&](size_t n) {
     uint8_t* p = base ? static_cast<uint8_t*>(base) + off : nullptr;
     off += align256(n);
     return p;
   };
-  w.qc = take(nq * 128);
-  w.qs = take(nq * 4);
   w.kc = take(nk * 128);
   w.ks = take(nk * 4);
   w.vc = take(nk * 128);
@@ -274,6 +273,29 @@ MXFA_EXPORT int mxfa_attn_fwd_fused(const uint8_t* qc, const uint8_t* qs, const 
                     "attn_fwd_fused launch");
 }
 
+MXFA_EXPORT int mxfa_attn_fwd_fused_bf16q(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const uint8_t* kc,
+                                          const uint8_t* ks, const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt,
+                                          const uint8_t* vta, int B, int S, int Hq, int Hkv, int D,
+                                          float softmax_scale, void* out, int64_t osb, int64_t oss, int64_t osh,
+                                          int out_dtype, float* lse_out, void* stream) {
+  g_last_error.clear();
+  TRY(check_attn_shape(B, S, Hq, Hkv, D));
+  TRY(check_view("q", q, B, S, Hq, qsb, qss, qsh, 8));
+  const char* n[] = {"kc", "ks", "vc", "vcs", "vt", "vta"};
+  const void* p[] = {kc, ks, vc, vcs, vt, vta};
+  TRY(check_ptrs(n, p, 6));
+  if (out_dtype != MXFA_OUT_BF16 && out_dtype != MXFA_OUT_F32)
+    return fail(MXFA_ERR_UNSUPPORTED, "unknown output dtype %d", out_dtype);
+  TRY(check_view("out", out, B, S, Hq, osb, oss, osh, out_dtype == MXFA_OUT_BF16 ? 8 : 4));
+  if (lse_out && !aligned16(lse_out)) return fail(MXFA_ERR_ALIGN, "lse_out is not 16-byte aligned");
+  TRY(check_device());
+  return hip_status(mxfa::launch_attn_fused(nullptr, nullptr, kc, ks, vc, vcs, vt, vta, B, S, Hq, Hkv, softmax_scale,
+                                            out, osb, oss, osh, out_dtype == MXFA_OUT_BF16, lse_out,
+                                            static_cast<hipStream_t>(stream), nullptr,
+                                            static_cast<const uint16_t*>(q), qsb, qss, qsh),
+                    "attn_fwd_fused_bf16q launch");
+}
+
 MXFA_EXPORT int mxfa_attn_fwd_fused_mxfp8(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                                           const uint8_t* ks, const uint8_t* vc, const uint8_t* vcs,
                                           const uint8_t* vt, const uint8_t* vta, int B, int S, int Hq, int Hkv,
@@ -339,12 +361,11 @@ MXFA_EXPORT int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t q
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t *q16 = static_cast<const uint16_t*>(q), *k16 = static_cast<const uint16_t*>(k),
                  *v16 = static_cast<const uint16_t*>(v);
-  TRY(hip_status(mxfa::launch_quantize_rowwise(q16, B, S, Hq, qsb, qss, qsh, w.qc, w.qs, st), "quantize q"));
   TRY(hip_status(mxfa::launch_quantize_rowwise(k16, B, S, Hkv, ksb, kss, ksh, w.kc, w.ks, st), "quantize k"));
   TRY(hip_status(mxfa::launch_quantize_v(v16, B, S, Hkv, vsb, vss, vsh, w.vc, w.vcs, w.vt, w.vta, st), "quantize v"));
-  return hip_status(mxfa::launch_attn_fused(w.qc, w.qs, w.kc, w.ks, w.vc, w.vcs, w.vt, w.vta, B, S, Hq, Hkv,
+  return hip_status(mxfa::launch_attn_fused(nullptr, nullptr, w.kc, w.ks, w.vc, w.vcs, w.vt, w.vta, B, S, Hq, Hkv,
                                            softmax_scale, out, osb, oss, osh, out_dtype == MXFA_OUT_BF16, lse_out,
-                                           st),
+                                           st, nullptr, q16, qsb, qss, qsh),
                     "fused attention");
 }
 

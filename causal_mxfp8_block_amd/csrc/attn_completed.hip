@@ -327,6 +327,8 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
 struct AttnParams {
   const uint8_t *qc, *qs, *kc, *ks, *vc, *vcs;  // rowwise Q/K and columnwise V codes/scales
   const uint8_t *vt, *vta;                       // token-normalised V (fused epilogue only)
+  const uint16_t* qbf;                           // fused only: bf16 Q view quantised in-kernel (else qc/qs)
+  int64_t qsb, qss, qsh;                         // ... its element strides
   int S, Hq, Hkv, n_qtiles;
   int n_pairs;                                   // B * Hq
   int xcd_pairs;                                 // n_pairs / 8 when n_pairs % 8 == 0, else 0
@@ -408,7 +410,49 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   // D-block 2m + hf.
   v8i qop[2] = {};
   int qsc[2] = {127, 127};
-  if (wave_valid) {
+  if (kFused && P.qbf) {
+    // Q quantised here from bf16, with the rowwise quantiser's rule (TE#3865 Description: Q in MXFP8
+    // with one E8M0 per 32 elements of D): lane (c, hf) holds, for step m, halves of D-blocks 2m
+    // (d = 64m + 16hf + [0,16)) and 2m + 1 (d = 64m + 32 + 16hf + [0,16)); the other halves are in lane
+    // c + 32(1 - hf), whose maxima complete the block amax. Same operations as the quantiser, so the
+    // codes and scales are identical to its output.
+    const int row = wave_valid ? qw + c : 0;
+    const uint16_t* xrow = P.qbf + b * P.qsb + (int64_t)row * P.qss + hq * P.qsh;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float v[2][16];
+      float am[2];
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const uint4* src = reinterpret_cast<const uint4*>(xrow + 64 * m + 32 * part + 16 * hf);
+        const uint4 r0 = src[0], r1 = src[1];
+        const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[part][2 * i] = bf16_to_f32(w[i] & 0xffffu);
+          v[part][2 * i + 1] = bf16_to_f32(w[i] >> 16);
+          a = fmaxf(a, fabsf(v[part][2 * i]));
+          a = fmaxf(a, fabsf(v[part][2 * i + 1]));
+        }
+        am[part] = fmaxf(a, __shfl_xor(a, 32));
+      }
+      uint32_t cw[8];
+      int kb[2];
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        kb[part] = e8m0_exponent(am[part]);
+        const float f = pow2_neg(kb[part]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          cw[4 * part + j] = pack4_e4m3(v[part][4 * j] * f, v[part][4 * j + 1] * f, v[part][4 * j + 2] * f,
+                                        v[part][4 * j + 3] * f);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qop[m][j] = (int)cw[j];
+      qsc[m] = (hf ? kb[1] : kb[0]) + 127;
+    }
+  } else if (wave_valid) {
     const uint8_t* qrow = P.qc + (bhq * S + qw + c) * 128;
     const uint32_t sw = *reinterpret_cast<const uint32_t*>(P.qs + (bhq * S + qw + c) * 4);
 #pragma unroll
@@ -714,8 +758,13 @@ hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uin
 hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                              const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B,
                              int S, int Hq, int Hkv, float softmax_scale, void* out, int64_t osb, int64_t oss,
-                             int64_t osh, int out_bf16, float* lse_out, hipStream_t stream, uint8_t* sf_o) {
+                             int64_t osh, int out_bf16, float* lse_out, hipStream_t stream, uint8_t* sf_o,
+                             const uint16_t* qbf, int64_t qsb, int64_t qss, int64_t qsh) {
   AttnParams p = base_params(qc, qs, kc, ks, vc, vcs, B, S, Hq, Hkv, softmax_scale);
+  p.qbf = qbf;
+  p.qsb = qsb;
+  p.qss = qss;
+  p.qsh = qsh;
   p.vt = vt;
   p.vta = vta;
   p.out = out;

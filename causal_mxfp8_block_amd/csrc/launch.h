@@ -24,7 +24,9 @@ hipError_t launch_attn_fused(const uint8_t* qc, const uint8_t* qs, const uint8_t
                              const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt, const uint8_t* vta, int B,
                              int S, int Hq, int Hkv, float softmax_scale, void* out, int64_t osb, int64_t oss,
                              int64_t osh, int out_bf16, float* lse_out, hipStream_t stream,
-                             uint8_t* sf_o = nullptr);  // sf_o != null: MXFP8 O codes into out
+                             uint8_t* sf_o = nullptr,  // sf_o != null: MXFP8 O codes into out
+                             const uint16_t* qbf = nullptr, int64_t qsb = 0, int64_t qss = 0,
+                             int64_t qsh = 0);  // qbf != null: bf16 Q view, quantised in-kernel (qc, qs unused)
 hipError_t launch_attn_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                              const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv, float softmax_scale,
                              void* out, int64_t osb, int64_t oss, int64_t osh, int out_bf16, float* lse_out,

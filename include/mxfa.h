@@ -137,12 +137,26 @@ int mxfa_attn_fwd_leaky(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                         float softmax_scale, void* out, int64_t osb, int64_t oss, int64_t osh, int out_dtype,
                         float* lse_out, void* stream);
 
-/* Bytes of workspace mxfa_attn_fwd needs (the MXFP8 codes and scales, 256-byte aligned parts). */
+/* Bytes of workspace mxfa_attn_fwd needs (the K and V MXFP8 codes and scales, 256-byte aligned parts). */
 size_t mxfa_attn_fwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D);
 
-/* attn_fwd -- the whole forward: the three quantisations, then attn_fwd_fused, in that order on
- * `stream`, using `workspace` (at least mxfa_attn_fwd_workspace_bytes, 256-byte aligned) for the
- * codes. q [B,S,Hq,D], k and v [B,S,Hkv,D] bf16 views; out is a [B,S,Hq,D] view. */
+/* attn_fwd_fused_bf16q -- attn_fwd_fused with Q given as its bf16 [B,S,Hq,D] view (strides qsb, qss,
+ * qsh, multiples of 8 elements) instead of its codes: each row of Q is quantised inside the attention
+ * kernel by the rule of mxfp8_quantize's rowwise mode (TE #3865 Description: Q in MXFP8 with one E8M0
+ * per 32 elements of D), giving the same codes and scales, so the output equals mxfp8_quantize
+ * followed by attn_fwd_fused bit for bit. This saves the separate pass over Q. Other arguments as
+ * attn_fwd_fused. */
+int mxfa_attn_fwd_fused_bf16q(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const uint8_t* kc,
+                              const uint8_t* ks, const uint8_t* vc, const uint8_t* vcs, const uint8_t* vt,
+                              const uint8_t* vta, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                              void* out, int64_t osb, int64_t oss, int64_t osh, int out_dtype, float* lse_out,
+                              void* stream);
+
+/* attn_fwd -- the whole forward: the K and V quantisations, then attn_fwd_fused_bf16q (which
+ * quantises Q in-kernel), in that order on `stream`, using `workspace` (at least
+ * mxfa_attn_fwd_workspace_bytes, 256-byte aligned) for the K and V codes. q [B,S,Hq,D], k and v
+ * [B,S,Hkv,D] bf16 views; out is a [B,S,Hq,D] view. The result equals the separate calls
+ * (mxfp8_quantize of Q, K and V, then attn_fwd_fused) bit for bit. */
 int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const void* k, int64_t ksb, int64_t kss,
                   int64_t ksh, const void* v, int64_t vsb, int64_t vss, int64_t vsh, int B, int S, int Hq, int Hkv,
                   int D, float softmax_scale, void* workspace, size_t workspace_bytes, void* out, int64_t osb,

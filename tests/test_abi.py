@@ -170,3 +170,20 @@ def test_fused_mxfp8_validation(args, status, needle):
                                                       a["D"], 0.1, a["o"], S * Hq * 128, a["oss"], 128, FAKE,
                                                       a["lse"], None))
     assert st == status and needle in msg, (st, msg)
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(D=64), 3, "D = 64"),
+    (dict(q=None), 1, "q is NULL"),
+    (dict(qsh=12), 4, "multiples of 8"),
+    (dict(vt=None), 1, "vt is NULL"),
+    (dict(dtype=3), 3, "output dtype"),
+])
+def test_fused_bf16q_validation(args, status, needle):
+    a = dict(D=128, q=FAKE, qsh=128, vt=FAKE, dtype=0)
+    a.update(args)
+    S, Hq = 64, 4
+    st, msg = _err(mx.lib().mxfa_attn_fwd_fused_bf16q(a["q"], S * Hq * 128, Hq * 128, a["qsh"], FAKE, FAKE, FAKE, FAKE,
+                                                      a["vt"], FAKE, 1, S, Hq, 2, a["D"], 0.1, FAKE, S * Hq * 128,
+                                                      Hq * 128, 128, a["dtype"], None, None))
+    assert st == status and needle in msg, (st, msg)

@@ -123,7 +123,8 @@ def test_bf16_output_is_rne_of_f32_output():
 
 
 def test_fused_entry_equals_attn_fwd_and_stepwise_path_matches_oracle():
-    """attn_fwd = quantise + attn_fwd_fused, bit for bit; the stepwise path (two partials and the
+    """attn_fwd (K, V quantised, Q inside the attention kernel) = quantise + attn_fwd_fused, bit for
+    bit; the stepwise path (two partials and the
     merge as separate kernels) and the fused one both meet the oracle."""
     inp = make_inputs(custom(2, 4, 1, 224, values="token_amplitudes", seed=12))
     w = inp.workload
@@ -143,6 +144,31 @@ def test_fused_entry_equals_attn_fwd_and_stepwise_path_matches_oracle():
         go = o_.double().cpu().numpy().transpose(0, 2, 1, 3)
         assert report(name, go, ro, rms, allowance=parts["allowance"], tol=TOL) <= TOL
         assert np.max(np.abs(l_.double().cpu().numpy() - rl)) < 1e-3
+
+
+@pytest.mark.parametrize("shape,layout,values", [((1, 1, 1, 128), "bshd", "outliers"),
+                                                  ((2, 4, 2, 416), "sbhd", "token_amplitudes"),
+                                                  ((1, 8, 2, 288), "bshd", "normal"),
+                                                  ((1, 3, 1, 96), "sbhd", "outliers")])
+def test_bf16q_entry_equals_quantise_then_fused(shape, layout, values):
+    """attn_fwd_fused_bf16q quantises Q inside the attention kernel: its output and LSE equal
+    mxfp8_quantize(q) followed by attn_fwd_fused bit for bit, in both output dtypes, also when Q is a
+    strided view (every other head of a wider tensor)."""
+    B, Hq, Hkv, S = shape
+    inp = make_inputs(custom(B, Hq, Hkv, S, layout=layout, values=values, seed=31 + S))
+    g = gpu_quantize(inp)
+    q = to_dev(inp.q)
+    wide = torch.zeros(q.shape[:2] + (2 * Hq, 128), dtype=q.dtype, device=q.device)
+    wide[:, :, ::2] = q
+    qv = wide[:, :, ::2]  # the same values through strides (element stride of a head: 256)
+    for dt in (torch.float32, torch.bfloat16):
+        ref, rl = mx.attn_fwd_fused(g["qc"], g["qs"], g["kc"], g["ks"], g["vc"], g["vcs"], g["vt"], g["vta"],
+                                    inp.workload.scale, out_dtype=dt, layout=layout)
+        for qq in (q, qv):
+            got, gl = mx.attn_fwd_fused_bf16q(qq, g["kc"], g["ks"], g["vc"], g["vcs"], g["vt"], g["vta"],
+                                              inp.workload.scale, out_dtype=dt, layout=layout)
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref) and torch.equal(gl, rl)
 
 
 def test_causality_every_t_tiny():
