@@ -143,6 +143,7 @@ mxfa::BwdWorkspace carve_bwd(void* base, int B, int S, int Hq, int Hkv) {
   w.gd = reinterpret_cast<uint16_t*>(take(nq));
   w.gdt = reinterpret_cast<uint16_t*>(take(nq));
   w.delta = reinterpret_cast<float*>(take((size_t)B * Hq * S * 4));
+  w.lse2 = reinterpret_cast<float*>(take((size_t)B * Hq * S * 4));
   w.bytes = off;
   return w;
 }

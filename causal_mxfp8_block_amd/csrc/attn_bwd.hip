@@ -54,16 +54,23 @@ __device__ __forceinline__ v8bf to_bf16(const v16f& x, int t) {
   return r;
 }
 
+// Position of query q (0..31) of a transposed dK/dV tile row: MFMA slot order, so that lane group g
+// reads queries 4g..4g+3 and 16+4g..16+4g+3 as one 16-byte operand (positions 8g..8g+7).
+__device__ __forceinline__ int dkdv_tpos(int q) { return 8 * ((q >> 2) & 3) + 4 * (q >> 4) + (q & 3); }
+
 // ---- preparation -------------------------------------------------------------------------------
 // One workgroup per (b, h, 64-token tile), 256 threads: thread g handles token g/4, columns
 // 32(g%4) .. +32. Source kSrc: 0 rowwise codes + E8M0 per 32 columns, 1 token-normalised codes + one
-// E8M0 amplitude per token, 2 a bf16 [B,S,H,D] view (with Delta from the o view when delta != null).
-// Writes the bf16 rows to out [B,H,S,D] and, when out_t != null, the transposed out_t [B,H,D,S].
-template <int kSrc>
+// E8M0 amplitude per token, 2 a bf16 [B,S,H,D] view (with Delta from the o view and lse * log2(e)
+// from lse when delta != null). Writes the bf16 rows to out [B,H,S,D] and, when out_t != null, the
+// transposed out_t [B,H,D,S]; with kSlot the tokens of each 32-token block of out_t are stored in the
+// dK/dV kernel's MFMA slot order (dkdv_tpos), so that its tiles load as contiguous 16-byte pieces.
+template <int kSrc, bool kSlot = false>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, const uint8_t* scales, const uint16_t* x,
                                                        int64_t sb, int64_t ss, int64_t sh, const uint16_t* o,
                                                        int64_t osb, int64_t oss, int64_t osh, int S, int H,
-                                                       uint16_t* out, uint16_t* out_t, float* delta) {
+                                                       uint16_t* out, uint16_t* out_t, float* delta,
+                                                       const float* lse = nullptr, float* lse2 = nullptr) {
   __shared__ __align__(16) uint16_t tile[64 * BW_ROW];
   const int g = threadIdx.x, tok = g >> 2, c0 = (g & 3) * 32;
   const int s0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
@@ -94,7 +101,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, con
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
-        if ((g & 3) == 0) delta[bh * S + s] = acc;
+        if ((g & 3) == 0) {
+          delta[bh * S + s] = acc;
+          lse2[bh * S + s] = lse[bh * S + s] * 1.4426950408889634f;
+        }
       }
     } else {
       const uint8_t* crow = codes + (bh * S + s) * 128 + c0;
@@ -129,8 +139,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, con
   if (s0 + t0 >= S) return;  // S % 32 == 0: a half tile is either wholly inside or wholly outside
   uint32_t p[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-    p[e] = (uint32_t)tile[(t0 + 2 * e) * BW_ROW + d] | ((uint32_t)tile[(t0 + 2 * e + 1) * BW_ROW + d] << 16);
+  for (int e = 0; e < 16; ++e) {
+    // tokens t0 + 2e and t0 + 2e + 1 stay one dword (dkdv_tpos keeps even-odd pairs together)
+    const int pos = kSlot ? (dkdv_tpos(2 * e) >> 1) : e;
+    p[pos] = (uint32_t)tile[(t0 + 2 * e) * BW_ROW + d] | ((uint32_t)tile[(t0 + 2 * e + 1) * BW_ROW + d] << 16);
+  }
   uint4* tdst = reinterpret_cast<uint4*>(out_t + (bh * 128 + d) * S + s0 + t0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) tdst[q] = make_uint4(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
@@ -139,6 +152,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, con
 struct BwdParams {
   const uint16_t *qd, *qdt, *kd, *kdt, *vd, *gd, *gdt;  // decoded operands (workspace)
   const float *lse, *delta;                              // [B,Hq,S]
+  const float* lse2;                                     // lse * log2(e), [B,Hq,S] (workspace)
   int S, Hq, Hkv;
   float scale, scale_log2;
   uint16_t *dq, *dk, *dv;                                // bf16 outputs (views)
@@ -177,15 +191,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v4f mfma16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// Position of query q (0..31) of a transposed dK/dV tile row: MFMA slot order, so that lane group g
-// reads queries 4g..4g+3 and 16+4g..16+4g+3 as one 16-byte operand (positions 8g..8g+7).
-__device__ __forceinline__ int dkdv_tpos(int q) { return 8 * ((q >> 2) & 3) + 4 * (q >> 4) + (q & 3); }
-__device__ __forceinline__ void store_col16_dkdv(uint16_t* dst, uint4 v, int t) {
-  // thread t: row d = t/4, queries q0 = 8(t%4) .. q0+7, in two halves of four
-  const int d = t >> 2, q0 = (t & 3) * 8;
-  uint16_t* row = dst + d * BW_TROW;
-  *reinterpret_cast<uint2*>(row + dkdv_tpos(q0)) = make_uint2(v.x, v.y);
-  *reinterpret_cast<uint2*>(row + dkdv_tpos(q0 + 4)) = make_uint2(v.z, v.w);
+// Global -> LDS without registers: lane l's 16 (or 4) bytes land at lds + 16 l (4 l); lds wave-uniform.
+__device__ __forceinline__ void gload_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, (__attribute__((address_space(3))) void*)lds,
+                                   16, 0, 0);
+}
+__device__ __forceinline__ void gload_lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, (__attribute__((address_space(3))) void*)lds,
+                                   4, 0, 0);
 }
 
 // Workgroup: 8 waves (two per SIMD) = keys 128 kt .. 128 kt + 127 of (b, hk); wave w owns keys
@@ -196,16 +209,19 @@ __device__ __forceinline__ void store_col16_dkdv(uint16_t* dst, uint4 v, int t) 
 // 32-wide steps), P and dS elementwise in the accumulators, then dV^T += dO^T P and dK^T += Q^T dS with
 // P and dS as the B operand straight from those accumulators (element i of row tile mt is query
 // 16mt + 4g + i: slot (g, e) of the contraction is query 16(e/4) + 4g + e%4, the order in which the
-// transposed tiles are stored). The next step's tiles are fetched into registers while the current
-// one computes, then stored into the other LDS buffer.
-constexpr int DKDV_NBUF = 3;  // LDS ring: the step computing, the next one (stored), the one after (arriving)
+// preparation pass stores the transposed copies). Each step's tiles go from global memory straight
+// into a ring of three LDS slots (loads with the LDS flag, no registers), two steps ahead.
+constexpr int DKDV_NBUF = 3;  // LDS ring: the step computing, the previous one (free), the one arriving
 struct DkdvTiles {
-  uint16_t q[32 * BW_ROW], g[32 * BW_ROW], qt[128 * BW_TROW], gt[128 * BW_TROW];
-  float l[32], d[32];
+  // Unpadded rows; reads stay conflict-free through XOR swizzles of the 16-byte chunks:
+  uint16_t q[32 * 128], g[32 * 128];    // Q, dO rows: chunk c of row r in slot c ^ (r & 15)
+  uint16_t qt[128 * 32], gt[128 * 32];  // Q^T, dO^T rows (slot order): chunk c of row d in slot c ^ ((d >> 2) & 3)
+  float l[32], d[32];                   // lse * log2(e) and Delta of the step's 32 queries
 };
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(const BwdParams P) {
   __shared__ __align__(16) DkdvTiles buf[DKDV_NBUF];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int G = P.Hq / P.Hkv;
   const int key0 = 128 * kt + 16 * wave;
@@ -225,39 +241,30 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
   const int nqb = S / 32, qb0 = 4 * kt, per_head = nqb - qb0, nsteps = G * per_head;
-  // Staging: thread t moves one 16-byte piece of each of Q, dO (row t/16, columns 8(t%16)..), Q^T and
-  // dO^T (row d = t/4, queries 8(t%4)..), and threads 0..31 the lse and Delta of query t.
-  // Two register sets alternate: the tiles of step st + 2 are fetched during step st and stored at its
-  // end, so each fetch has two steps of time to arrive.
-  uint4 rq, rg, rqt, rgt, rq2, rg2, rqt2, rgt2;
-  float rl = 0.f, rd = 0.f, rl2 = 0.f, rd2 = 0.f;
-  const int rrow = tid >> 4, rcol = (tid & 15) * 8, tdd = tid >> 2, tq0 = (tid & 3) * 8;
-#define DKDV_FETCH(n_, RQ, RG, RQT, RGT, RL, RD)                                           \
-  do {                                                                                     \
-    const int hq_ = hk * G + (n_) / per_head, q0_ = 32 * (nqb - 1 - (n_) % per_head);      \
-    const int64_t bhq_ = (int64_t)b * P.Hq + hq_;                                          \
-    RQ = *reinterpret_cast<const uint4*>(P.qd + (bhq_ * S + q0_ + rrow) * 128 + rcol);     \
-    RG = *reinterpret_cast<const uint4*>(P.gd + (bhq_ * S + q0_ + rrow) * 128 + rcol);     \
-    RQT = *reinterpret_cast<const uint4*>(P.qdt + (bhq_ * 128 + tdd) * S + q0_ + tq0);     \
-    RGT = *reinterpret_cast<const uint4*>(P.gdt + (bhq_ * 128 + tdd) * S + q0_ + tq0);     \
-    if (tid < 32) {                                                                        \
-      RL = P.lse[bhq_ * S + q0_ + tid] * 1.4426950408889634f;                              \
-      RD = P.delta[bhq_ * S + q0_ + tid];                                                  \
-    }                                                                                      \
-  } while (0)
-#define DKDV_PUT(t_, RQ, RG, RQT, RGT, RL, RD)                               \
-  do {                                                                       \
-    *reinterpret_cast<uint4*>((t_).q + rrow * BW_ROW + rcol) = RQ;           \
-    *reinterpret_cast<uint4*>((t_).g + rrow * BW_ROW + rcol) = RG;           \
-    store_col16_dkdv((t_).qt, RQT, tid);                                     \
-    store_col16_dkdv((t_).gt, RGT, tid);                                     \
-    if (tid < 32) {                                                          \
-      (t_).l[tid] = RL;                                                      \
-      (t_).d[tid] = RD;                                                      \
-    }                                                                        \
-  } while (0)
-  // One step's compute on the tiles in T (step st): S, dP, P, dS, and the dV^T, dK^T updates.
-  auto dkdv_compute = [&](const DkdvTiles& T, int st) {
+  // Thread tid fills LDS chunk tid (16 bytes) of each of the four tiles: of Q and dO, row r = tid/16,
+  // slot tid%16, holding chunk (tid%16) ^ (r & 15) of that query's row; of Q^T and dO^T, row
+  // d = tid/4, slot tid%4, holding chunk (tid%4) ^ ((d >> 2) & 3) of the block's 64 bytes of row d.
+  // Wave 0 also moves the 32 lse * log2(e) and 32 Delta values (4 bytes per lane).
+  const int rr = tid >> 4, rx = (tid & 15) ^ (rr & 15), td = tid >> 2, tx = (tid & 3) ^ ((td >> 2) & 3);
+  auto fetch = [&](int n_, DkdvTiles& T) {
+    const int hq_ = hk * G + n_ / per_head, q0_ = 32 * (nqb - 1 - n_ % per_head);
+    const int64_t bhq_ = (int64_t)b * P.Hq + hq_;
+    gload_lds16(P.qd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T.q) + 1024 * wave_u);
+    gload_lds16(P.gd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T.g) + 1024 * wave_u);
+    gload_lds16(P.qdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T.qt) + 1024 * wave_u);
+    gload_lds16(P.gdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T.gt) + 1024 * wave_u);
+    if (wave_u == 0)
+      gload_lds4(lane < 32 ? P.lse2 + bhq_ * S + q0_ + lane : P.delta + bhq_ * S + q0_ + lane - 32, T.l);
+  };
+  fetch(0, buf[0]);
+  if (nsteps > 1) fetch(1, buf[1]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    // step st + 2 into the slot of step st - 1, which no wave reads after the barrier that ended it
+    if (st + 2 < nsteps) fetch(st + 2, buf[(st + 2) % DKDV_NBUF]);
+    __builtin_amdgcn_sched_barrier(0);
+    const DkdvTiles& T = buf[st % DKDV_NBUF];
     const int qb = nqb - 1 - st % per_head;
     {  // every wave computes every step (branch-free); key > query is masked below
       v4f sacc[2], pacc[2];
@@ -266,8 +273,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         v8bf qa[4], ga[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          qa[s] = ld8bf(T.q + (16 * mt + n) * BW_ROW + 32 * s + 8 * g);
-          ga[s] = ld8bf(T.g + (16 * mt + n) * BW_ROW + 32 * s + 8 * g);
+          const int off = (16 * mt + n) * 128 + 8 * ((4 * s + g) ^ n);  // row 16mt + n: (row & 15) = n
+          qa[s] = ld8bf(T.q + off);
+          ga[s] = ld8bf(T.g + off);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) sacc[mt][i] = pacc[mt][i] = 0.f;
@@ -301,37 +309,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       // dV^T += dO^T P and dK^T += Q^T dS: one MFMA per 16-row tile of D (K = the 32 queries)
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const v8bf gta = ld8bf(T.gt + (16 * dt + n) * BW_TROW + 8 * g);
-        const v8bf qta = ld8bf(T.qt + (16 * dt + n) * BW_TROW + 8 * g);
-        dvT[dt] = mfma16(gta, pb, dvT[dt]);
-        dkT[dt] = mfma16(qta, sb, dkT[dt]);
+        const int off = (16 * dt + n) * 32 + 8 * (g ^ ((n >> 2) & 3));  // row 16dt + n
+        dvT[dt] = mfma16(ld8bf(T.gt + off), pb, dvT[dt]);
+        dkT[dt] = mfma16(ld8bf(T.qt + off), sb, dkT[dt]);
       }
     }
-  };
-  DKDV_FETCH(0, rq, rg, rqt, rgt, rl, rd);
-  DKDV_PUT(buf[0], rq, rg, rqt, rgt, rl, rd);
-  if (nsteps > 1) DKDV_FETCH(1, rq, rg, rqt, rgt, rl, rd);  // set A: step 1, stored at the end of step 0
-  __syncthreads();
-  // Step st computes from slot st % 3. During it the tiles of step st + 2 are fetched into the register
-  // set that does not hold step st + 1; at its end step st + 1's tiles are stored into slot (st + 1) % 3,
-  // last read by step st - 2, two barriers earlier. The loop is unrolled by two so that the two
-  // register sets keep fixed roles.
-#define DKDV_STEP(st, FQ, FG, FQT, FGT, FL, FD, PQ, PG, PQT, PGT, PL, PD) \
-  do {                                                                   \
-    if ((st) + 2 < nsteps) DKDV_FETCH((st) + 2, FQ, FG, FQT, FGT, FL, FD); \
-    __builtin_amdgcn_sched_barrier(0);                                   \
-    dkdv_compute(buf[(st) % DKDV_NBUF], (st));                           \
-    __builtin_amdgcn_sched_barrier(0);                                   \
-    if ((st) + 1 < nsteps) DKDV_PUT(buf[((st) + 1) % DKDV_NBUF], PQ, PG, PQT, PGT, PL, PD); \
-    __syncthreads();                                                     \
-  } while (0)
-  for (int st = 0; st < nsteps; st += 2) {
-    DKDV_STEP(st, rq2, rg2, rqt2, rgt2, rl2, rd2, rq, rg, rqt, rgt, rl, rd);
-    if (st + 1 < nsteps) DKDV_STEP(st + 1, rq, rg, rqt, rgt, rl, rd, rq2, rg2, rqt2, rgt2, rl2, rd2);
+    __builtin_amdgcn_sched_barrier(0);
+    // The loads issued at the top of this step (step st + 2) complete here; the barrier publishes them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   }
-#undef DKDV_STEP
-#undef DKDV_FETCH
-#undef DKDV_PUT
   if (!valid) return;
   // lane (key n, g), element i of tile dt: column 16dt + 4g + i
   const int64_t off = b * P.ksb + (int64_t)(key0 + n) * P.kss + hk * P.ksh + 4 * g;
@@ -467,15 +454,16 @@ hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* 
                            uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream) {
   const dim3 tq((unsigned)((S + 63) / 64), (unsigned)Hq, (unsigned)B), tk((unsigned)((S + 63) / 64), (unsigned)Hkv,
                                                                           (unsigned)B);
-  bwd_prep_kernel<0><<<tq, 256, 0, stream>>>(qc, qs, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hq, ws.qd, ws.qdt, nullptr);
+  bwd_prep_kernel<0, true><<<tq, 256, 0, stream>>>(qc, qs, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hq, ws.qd, ws.qdt,
+                                                   nullptr);
   bwd_prep_kernel<0><<<tk, 256, 0, stream>>>(kc, ks, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.kd, ws.kdt, nullptr);
   bwd_prep_kernel<1><<<tk, 256, 0, stream>>>(vt, vta, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.vd, nullptr,
                                              nullptr);
-  bwd_prep_kernel<2><<<tq, 256, 0, stream>>>(nullptr, nullptr, dout, qsb, qss, qsh, o, qsb, qss, qsh, S, Hq, ws.gd,
-                                             ws.gdt, ws.delta);
+  bwd_prep_kernel<2, true><<<tq, 256, 0, stream>>>(nullptr, nullptr, dout, qsb, qss, qsh, o, qsb, qss, qsh, S, Hq,
+                                                   ws.gd, ws.gdt, ws.delta, lse, ws.lse2);
   BwdParams p{};
   p.qd = ws.qd; p.qdt = ws.qdt; p.kd = ws.kd; p.kdt = ws.kdt; p.vd = ws.vd; p.gd = ws.gd; p.gdt = ws.gdt;
-  p.lse = lse; p.delta = ws.delta;
+  p.lse = lse; p.delta = ws.delta; p.lse2 = ws.lse2;
   p.S = S; p.Hq = Hq; p.Hkv = Hkv;
   p.scale = softmax_scale;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);

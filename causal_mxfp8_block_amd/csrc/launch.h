@@ -9,6 +9,7 @@ namespace mxfa {
 struct BwdWorkspace {
   uint16_t *qd, *qdt, *kd, *kdt, *vd, *gd, *gdt;  // [B,H,S,128] and [B,H,128,S]
   float* delta;                                     // [B,Hq,S]
+  float* lse2;                                      // lse * log2(e), [B,Hq,S]
   size_t bytes;
 };
 

@@ -163,7 +163,7 @@ int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const vo
                   int64_t oss, int64_t osh, int out_dtype, float* lse_out, void* stream);
 
 /* Bytes of workspace mxfa_attn_bwd needs (decoded operands: 5 bf16 copies of [B,Hq,S,D] and 3 of
- * [B,Hkv,S,D], plus [B,Hq,S] fp32; 256-byte aligned parts). */
+ * [B,Hkv,S,D], plus two [B,Hq,S] fp32 arrays; 256-byte aligned parts). */
 size_t mxfa_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D);
 
 /* attn_bwd -- backward on decoded operands (TE #3865, Description, backward bullet: BF16 backward on
