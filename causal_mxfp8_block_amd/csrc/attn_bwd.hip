@@ -24,9 +24,10 @@
 //  * Key > query is masked to P = 0. The loops start at the workgroup's first block on or below the
 //    diagonal, so a wave whose own blocks start later computes at most three fully masked steps; that
 //    keeps the loop branch-free per wave.
-//  * Query (dK/dV) and key (dQ) blocks are staged in LDS per workgroup of 4 waves, double-buffered
-//    (the next step's tiles are fetched into registers while the current one computes), rows
-//    padded so that the 16- and 8-byte operand reads are bank-conflict-free.
+//  * Query (dK/dV) and key (dQ) blocks go from global memory straight into an LDS ring shared by the
+//    workgroup (loads with the LDS flag, issued a step or two ahead; no register staging). Rows are
+//    unpadded and the 16-byte chunks XOR-swizzled, so the operand reads are bank-conflict-free; the
+//    preparation pass writes the transposed copies in each kernel's MFMA slot order.
 #include "device_common.h"
 #include "launch.h"
 
@@ -34,11 +35,7 @@ namespace mxfa {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int BW_ROW = 136;  // LDS pitch (bf16) of a [token][D] tile row: 128 + 8 pad
-// LDS pitch (bf16) of a [D][32 tokens] tile row: 32 + 8 pad (rows 16-byte aligned, conflict-free 16-byte
-// reads). Within each 16-token group the tokens are stored in MFMA slot order: token u at position u with
-// bits 2 and 3 swapped, so one 16-byte read at 8h gives tokens 4h..4h+3 and 8+4h..8+4h+3.
-constexpr int BW_TROW = 40;
+constexpr int BW_ROW = 136;  // LDS pitch (bf16) of the preparation pass's [token][D] tile: 128 + 8 pad
 
 __device__ __forceinline__ v8bf ld8bf(const uint16_t* p) {  // 16 bytes, 16-byte aligned
   return __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(p));
@@ -57,15 +54,19 @@ __device__ __forceinline__ v8bf to_bf16(const v16f& x, int t) {
 // Position of query q (0..31) of a transposed dK/dV tile row: MFMA slot order, so that lane group g
 // reads queries 4g..4g+3 and 16+4g..16+4g+3 as one 16-byte operand (positions 8g..8g+7).
 __device__ __forceinline__ int dkdv_tpos(int q) { return 8 * ((q >> 2) & 3) + 4 * (q >> 4) + (q & 3); }
+// Same for the dQ kernel's 32x32 operands: within each 16-token half, bits 2 and 3 swapped, so that lane
+// half h reads tokens 4h..4h+3 and 8+4h..8+4h+3 of the half as one 16-byte operand.
+__device__ __forceinline__ int dq_tpos(int q) { return (q & 16) | ((q & 4) << 1) | ((q & 8) >> 1) | (q & 3); }
 
 // ---- preparation -------------------------------------------------------------------------------
 // One workgroup per (b, h, 64-token tile), 256 threads: thread g handles token g/4, columns
 // 32(g%4) .. +32. Source kSrc: 0 rowwise codes + E8M0 per 32 columns, 1 token-normalised codes + one
 // E8M0 amplitude per token, 2 a bf16 [B,S,H,D] view (with Delta from the o view and lse * log2(e)
 // from lse when delta != null). Writes the bf16 rows to out [B,H,S,D] and, when out_t != null, the
-// transposed out_t [B,H,D,S]; with kSlot the tokens of each 32-token block of out_t are stored in the
-// dK/dV kernel's MFMA slot order (dkdv_tpos), so that its tiles load as contiguous 16-byte pieces.
-template <int kSrc, bool kSlot = false>
+// transposed out_t [B,H,D,S]; with kSlot 1 (2) the tokens of each 32-token block of out_t are stored in
+// the dK/dV (dQ) kernel's MFMA slot order, dkdv_tpos (dq_tpos), so that its tiles load as contiguous
+// 16-byte pieces.
+template <int kSrc, int kSlot = 0>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, const uint8_t* scales, const uint16_t* x,
                                                        int64_t sb, int64_t ss, int64_t sh, const uint16_t* o,
                                                        int64_t osb, int64_t oss, int64_t osh, int S, int H,
@@ -140,8 +141,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, con
   uint32_t p[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    // tokens t0 + 2e and t0 + 2e + 1 stay one dword (dkdv_tpos keeps even-odd pairs together)
-    const int pos = kSlot ? (dkdv_tpos(2 * e) >> 1) : e;
+    // tokens t0 + 2e and t0 + 2e + 1 stay one dword (both orders keep even-odd pairs together)
+    const int pos = kSlot == 1 ? (dkdv_tpos(2 * e) >> 1) : kSlot == 2 ? (dq_tpos(2 * e) >> 1) : e;
     p[pos] = (uint32_t)tile[(t0 + 2 * e) * BW_ROW + d] | ((uint32_t)tile[(t0 + 2 * e + 1) * BW_ROW + d] << 16);
   }
   uint4* tdst = reinterpret_cast<uint4*>(out_t + (bh * 128 + d) * S + s0 + t0);
@@ -158,31 +159,6 @@ struct BwdParams {
   uint16_t *dq, *dk, *dv;                                // bf16 outputs (views)
   int64_t qsb, qss, qsh, ksb, kss, ksh;                 // strides of dq and of dk/dv
 };
-
-// Tile staging, split into the global loads (into registers, issued a step ahead) and the LDS stores.
-// Thread tid moves two 16-byte pieces i = 0, 1 of each tile.
-// Rows: a 32-token x 128 block (rows t0..t0+31 of a [S][128] bf16 head).
-__device__ __forceinline__ uint4 load_row16(const uint16_t* src, int t0, int tid, int i) {
-  const int idx = tid + 256 * i, row = idx >> 4, col = (idx & 15) * 8;
-  return *reinterpret_cast<const uint4*>(src + (int64_t)(t0 + row) * 128 + col);
-}
-__device__ __forceinline__ void store_row16(uint16_t* dst, uint4 v, int tid, int i) {
-  const int idx = tid + 256 * i, row = idx >> 4, col = (idx & 15) * 8;
-  *reinterpret_cast<uint4*>(dst + row * BW_ROW + col) = v;
-}
-// Columns: the 128 x 32-token block (columns t0..t0+31 of a [128][S] transposed head).
-__device__ __forceinline__ uint4 load_col16(const uint16_t* src, int S, int t0, int tid, int i) {
-  const int idx = tid + 256 * i, d = idx >> 2, col = (idx & 3) * 8;
-  return *reinterpret_cast<const uint4*>(src + (int64_t)d * S + t0 + col);
-}
-__device__ __forceinline__ void store_col16(uint16_t* dst, uint4 v, int tid, int i) {
-  // tokens col..col+3 and col+4..col+7 (col % 8 == 0) go to their slot-order positions
-  const int idx = tid + 256 * i, d = idx >> 2, col = (idx & 3) * 8;
-  const int lo = (col & 16) + ((col & 8) >> 1);
-  uint16_t* row = dst + d * BW_TROW;
-  *reinterpret_cast<uint2*>(row + lo) = make_uint2(v.x, v.y);
-  *reinterpret_cast<uint2*>(row + lo + 8) = make_uint2(v.z, v.w);
-}
 
 // ---- dK, dV ------------------------------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16 (operand layout probed): A lane (m = l%16, g = l/16) element e <-> A[m][8g+e];
@@ -336,13 +312,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
 // ---- dQ ----------------------------------------------------------------------------------------
 // Workgroup: 4 waves = queries 128 qt .. 128 qt + 127 of (b, hq); wave w owns queries 32(4qt + w) + [0, 32).
-// Key blocks staged double-buffered as in the dK/dV kernel.
+// Key blocks go from global memory straight into two LDS slots (loads with the LDS flag), one step
+// ahead, as in the dK/dV kernel.
 struct DqTiles {
-  uint16_t k[32 * BW_ROW], v[32 * BW_ROW], kt[128 * BW_TROW];
+  uint16_t k[32 * 128], v[32 * 128];  // K, V rows: chunk c of row r in slot c ^ (r & 15)
+  uint16_t kt[128 * 32];              // K^T rows (dQ slot order): chunk c of row d in slot c ^ ((d >> 2) & 3)
 };
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams P) {
   __shared__ __align__(16) DqTiles buf[2];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int hk = hq / (P.Hq / P.Hkv);
   const int qb = 4 * qt + wave, q0 = 32 * qb;
@@ -364,30 +343,24 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int i = 0; i < 16; ++i) dqT[dt][i] = 0.f;
   const uint16_t *kd = P.kd + bhk * S * 128, *vd = P.vd + bhk * S * 128, *kdt = P.kdt + bhk * 128 * S;
   const int nkb = min(4 * qt + 3, S / 32 - 1) + 1;  // key blocks any wave of the workgroup needs
-  uint4 rk0, rk1, rv0, rv1, rkt0, rkt1;
-#define DQ_FETCH(kb)                                \
-  do {                                              \
-    rk0 = load_row16(kd, 32 * (kb), tid, 0);        \
-    rk1 = load_row16(kd, 32 * (kb), tid, 1);        \
-    rv0 = load_row16(vd, 32 * (kb), tid, 0);        \
-    rv1 = load_row16(vd, 32 * (kb), tid, 1);        \
-    rkt0 = load_col16(kdt, S, 32 * (kb), tid, 0);   \
-    rkt1 = load_col16(kdt, S, 32 * (kb), tid, 1);   \
-  } while (0)
-#define DQ_PUT(t)                    \
-  do {                               \
-    store_row16(t.k, rk0, tid, 0);   \
-    store_row16(t.k, rk1, tid, 1);   \
-    store_row16(t.v, rv0, tid, 0);   \
-    store_row16(t.v, rv1, tid, 1);   \
-    store_col16(t.kt, rkt0, tid, 0); \
-    store_col16(t.kt, rkt1, tid, 1); \
-  } while (0)
-  DQ_FETCH(0);
-  DQ_PUT(buf[0]);
+  // Thread tid fills LDS chunks ci = tid + 256 i (i = 0, 1; 16 bytes each) of the three tiles: of K and
+  // V, row ci/16, slot ci%16; of K^T, row ci/4, slot ci%4; each wave's 64 chunks are contiguous.
+  auto fetch = [&](int kb, DqTiles& T) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ci = tid + 256 * i, r = ci >> 4, x = (ci & 15) ^ (r & 15), d = ci >> 2, xt = (ci & 3) ^ ((d >> 2) & 3);
+      const int lo = 16 * (256 * i + 64 * wave_u);
+      gload_lds16(kd + (int64_t)(32 * kb + r) * 128 + 8 * x, reinterpret_cast<uint8_t*>(T.k) + lo);
+      gload_lds16(vd + (int64_t)(32 * kb + r) * 128 + 8 * x, reinterpret_cast<uint8_t*>(T.v) + lo);
+      gload_lds16(kdt + (int64_t)d * S + 32 * kb + 8 * xt, reinterpret_cast<uint8_t*>(T.kt) + lo);
+    }
+  };
+  fetch(0, buf[0]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) DQ_FETCH(kb + 1);
+    // the next key block into the other slot, read last in step kb - 1 (before the barrier ending it)
+    if (kb + 1 < nkb) fetch(kb + 1, buf[(kb + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
     const DqTiles& T = buf[kb & 1];
     {  // branch-free as in the dK/dV kernel
@@ -395,8 +368,9 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       v8bf ka[8], va[8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        ka[s] = ld8bf(T.k + c * BW_ROW + 16 * s + 8 * h);
-        va[s] = ld8bf(T.v + c * BW_ROW + 16 * s + 8 * h);
+        const int off = c * 128 + 8 * ((2 * s + h) ^ (c & 15));  // columns 16s + 8h: chunk 2s + h
+        ka[s] = ld8bf(T.k + off);
+        va[s] = ld8bf(T.v + off);
       }
       v16f sacc, pacc;
 #pragma unroll
@@ -410,7 +384,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) kta[t][dt] = ld8bf(T.kt + (32 * dt + c) * BW_TROW + 16 * t + 8 * h);
+        for (int dt = 0; dt < 4; ++dt)  // row 32dt + c, chunk 2t + h
+          kta[t][dt] = ld8bf(T.kt + (32 * dt + c) * 32 + 8 * ((2 * t + h) ^ ((c >> 2) & 3)));
       const int qoff = 32 * (qb - kb);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -419,7 +394,8 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         if (kk > qoff + c) p = 0.f;  // key after query (whole block when kb > qb)
         pacc[i] = p * (pacc[i] - del);  // dS^T
       }
-      // dQ^T += K^T dS^T over the 32 keys, two 16-key steps (slot order as in the dK/dV kernel)
+      // dQ^T += K^T dS^T over the 32 keys, two 16-key steps: B slot (h, e) of step t is accumulator
+      // element 8t + e, key 16t + 8(e/4) + 4h + e%4, the order (dq_tpos) of the K^T tile's rows
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const v8bf sb = to_bf16(pacc, t);
@@ -428,12 +404,10 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + 1 < nkb) DQ_PUT(buf[(kb + 1) & 1]);
+    // The next key block's loads complete here; the barrier publishes them.
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
-#undef DQ_FETCH
-#undef DQ_PUT
   if (!valid) return;
   const int64_t off = b * P.qsb + (int64_t)(q0 + c) * P.qss + hq * P.qsh + 4 * h;
 #pragma unroll
@@ -454,12 +428,12 @@ hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* 
                            uint16_t* dq, uint16_t* dk, uint16_t* dv, hipStream_t stream) {
   const dim3 tq((unsigned)((S + 63) / 64), (unsigned)Hq, (unsigned)B), tk((unsigned)((S + 63) / 64), (unsigned)Hkv,
                                                                           (unsigned)B);
-  bwd_prep_kernel<0, true><<<tq, 256, 0, stream>>>(qc, qs, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hq, ws.qd, ws.qdt,
+  bwd_prep_kernel<0, 1><<<tq, 256, 0, stream>>>(qc, qs, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hq, ws.qd, ws.qdt,
                                                    nullptr);
-  bwd_prep_kernel<0><<<tk, 256, 0, stream>>>(kc, ks, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.kd, ws.kdt, nullptr);
+  bwd_prep_kernel<0, 2><<<tk, 256, 0, stream>>>(kc, ks, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.kd, ws.kdt, nullptr);
   bwd_prep_kernel<1><<<tk, 256, 0, stream>>>(vt, vta, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.vd, nullptr,
                                              nullptr);
-  bwd_prep_kernel<2, true><<<tq, 256, 0, stream>>>(nullptr, nullptr, dout, qsb, qss, qsh, o, qsb, qss, qsh, S, Hq,
+  bwd_prep_kernel<2, 1><<<tq, 256, 0, stream>>>(nullptr, nullptr, dout, qsb, qss, qsh, o, qsb, qss, qsh, S, Hq,
                                                    ws.gd, ws.gdt, ws.delta, lse, ws.lse2);
   BwdParams p{};
   p.qd = ws.qd; p.qdt = ws.qdt; p.kd = ws.kd; p.kdt = ws.kdt; p.vd = ws.vd; p.gd = ws.gd; p.gdt = ws.gdt;
