@@ -26,11 +26,13 @@
 //    the block-scaled FP8 MFMA again, on the columnwise V codes (keys contiguous per column).
 //  * O^T leaves one query per lane too, so the rescale and the final 1/l are per-lane scalars.
 //  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the LDS flag), once per
-//    workgroup, shared by the 4 waves: a ring of three tiles, one barrier per tile. No register holds
+//    workgroup, shared by the 4 waves: a ring of four tiles, one barrier per tile. No register holds
 //    a tile in flight.
 //  * Software pipeline: while a wave runs the softmax of tile n, it issues the four score MFMAs of
-//    tile n + 1, one per group of exponentials, so the matrix core works beside the VALU within the
-//    wave; tile n + 2 arrives meanwhile. The ordinary causal variant keeps a plain loop.
+//    tile n + 1 and the four P.V MFMAs of tile n - 1, one of each per group of exponentials, so the
+//    matrix core works beside the VALU within the wave; tile n + 2 arrives meanwhile. A deferred P
+//    block stays exact across a rescale: its E8M0 byte drops by the same power of two. The ordinary
+//    causal variant keeps a plain loop.
 //  * Two workgroups per CU (two waves per SIMD, up to 254 VGPRs each): the softmax VALU work of one
 //    wave also overlaps the MFMAs and memory waits of the other.
 //  * Full tiles and the half tile at the end of a wave's range are separate code paths, so the
@@ -203,12 +205,17 @@ __device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const
 // softmax computes, so the matrix core works on them while this wave's VALU runs the softmax: one
 // MFMA per group of exponentials. kMaskBlk (ordinary causal variant only, with kNext = 0): that block
 // is the wave's own 32-token block, of which query qw + c sees keys qw .. qw + c; the others get
-// p = 0, and its E8M0 comes from the visible keys.
-template <bool kFull, int kNext = 0, int kMaskBlk = -1>
+// p = 0, and its E8M0 comes from the visible keys. kDefer: this tile's P.V is not issued here but
+// handed out in (pprev, sprev); the previous tile's, handed in the same way, is issued here, one
+// MFMA per group of exponentials, on the V of tp (zero codes, which add exactly 0, when there is
+// no previous tile). With kDefer the matrix core runs beside the VALU for all eight MFMAs of a
+// tile, and no P.V waits at the end of the softmax.
+template <bool kFull, int kNext = 0, int kMaskBlk = -1, bool kDefer = false>
 __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const TileSmem& t, v16f (&snext)[2],
-                                           const TileSmem& tn, const v8i (&qop)[2], const int (&qsc)[2],
-                                           float scale_log2, int c, int hf, bool first) {
-  static_assert(kMaskBlk < 0 || kNext == 0, "the masked own block is the wave's last tile");
+                                           const TileSmem& tn, const TileSmem& tp, v8i& pprev, int& sprev,
+                                           const v8i (&qop)[2], const int (&qsc)[2], float scale_log2, int c,
+                                           int hf, bool first) {
+  static_assert(kMaskBlk < 0 || (kNext == 0 && !kDefer), "the masked own block is the wave's last tile");
   constexpr int nmf = 2 * kNext;  // score MFMAs of the next tile: (kt, m) = (0,0), (1,0), (0,1), (1,1)
   // Lane (c, hf), element i of block kt holds key 32kt + 16hf + i of the tile, query c.
   if (kMaskBlk >= 0) {
@@ -238,6 +245,7 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
   // This tile's V^T operands: lane (c, hf), tile dt: column 32dt + c, keys 16hf + [0,16) and
   // 32 + 16hf + [0,16). Read here when no next-tile scores are due (their latency hides under the
   // softmax), else in the last group, once the K operands are consumed (register pressure).
+  // With kDefer, the V^T operand of the previous tile's P.V MFMA dt, read one group before its use.
   v8i vop[4];
   uint32_t vsw;
   auto vread = [&]() {
@@ -250,7 +258,19 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     }
     vsw = *reinterpret_cast<const uint32_t*>(t.vs + hf * 128 + c * 4);
   };
-  if (nmf == 0) vread();
+  auto vread_prev = [&](int dt) {
+    const int d = 32 * dt + c;
+    const uint8_t* vr = tp.v + d * CB_VROW;
+    return make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
+                    *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
+  };
+  v8i vcur{};
+  if (kDefer) {
+    vsw = *reinterpret_cast<const uint32_t*>(tp.vs + hf * 128 + c * 4);
+    vcur = vread_prev(0);
+  } else if (nmf == 0) {
+    vread();
+  }
 
   float m0 = sacc[0][0], m1 = kFull ? sacc[1][0] : -INFINITY;
 #pragma unroll
@@ -273,6 +293,8 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
       for (int i = 0; i < 16; ++i) st.o[dt][i] *= f;
     st.lsum *= f;
     st.T += shift;
+    // a deferred P block was coded against the old T: its E8M0 byte drops by the same shift
+    if (kDefer) sprev = max(sprev - (int)shift, 1);
     negT = -st.T;
     pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
     pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
@@ -293,7 +315,16 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
                          : mfma_mx<1, 0>(kcur, qop[1], snext[kt], ksc[kt], qsc[1]);
       if (g + 1 < nmf) knext = kread(g + 1);
     }
-    if (nmf > 0 && g == 3) vread();
+    if (kDefer) {  // P.V MFMA g of the previous tile
+      const v8i vnx = g < 3 ? vread_prev(g + 1) : v8i{};
+      if (g == 0) st.o[0] = mfma_mx<0, 0>(vcur, pprev, st.o[0], (int)vsw, sprev);
+      if (g == 1) st.o[1] = mfma_mx<1, 0>(vcur, pprev, st.o[1], (int)vsw, sprev);
+      if (g == 2) st.o[2] = mfma_mx<2, 0>(vcur, pprev, st.o[2], (int)vsw, sprev);
+      if (g == 3) st.o[3] = mfma_mx<3, 0>(vcur, pprev, st.o[3], (int)vsw, sprev);
+      vcur = vnx;
+    } else if (nmf > 0 && g == 3) {
+      vread();
+    }
     float q[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[0][4 * g + e], scale_log2, nb0));
@@ -318,10 +349,33 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
   }
   st.lsum += kFull ? ldexpf(ls0, e0 - 127) + ldexpf(ls1, e1 - 127) : ldexpf(ls0, e0 - 127);
   const int psc = hf ? e1 : e0;
+  if (kDefer) {  // this tile's P.V goes to the next iteration
+    pprev = pop;
+    sprev = psc;
+    return;
+  }
   st.o[0] = mfma_mx<0, 0>(vop[0], pop, st.o[0], (int)vsw, psc);
   st.o[1] = mfma_mx<1, 0>(vop[1], pop, st.o[1], (int)vsw, psc);
   st.o[2] = mfma_mx<2, 0>(vop[2], pop, st.o[2], (int)vsw, psc);
   st.o[3] = mfma_mx<3, 0>(vop[3], pop, st.o[3], (int)vsw, psc);
+}
+
+// A deferred P.V (the last one of a wave), on the V of tile tp.
+__device__ __forceinline__ void pv_deferred(RowState& st, const TileSmem& tp, const v8i& pprev, int sprev, int c,
+                                            int hf) {
+  const uint32_t vsw = *reinterpret_cast<const uint32_t*>(tp.vs + hf * 128 + c * 4);
+  v8i vop[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + c;
+    const uint8_t* vr = tp.v + d * CB_VROW;
+    vop[dt] = make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
+                       *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
+  }
+  st.o[0] = mfma_mx<0, 0>(vop[0], pprev, st.o[0], (int)vsw, sprev);
+  st.o[1] = mfma_mx<1, 0>(vop[1], pprev, st.o[1], (int)vsw, sprev);
+  st.o[2] = mfma_mx<2, 0>(vop[2], pprev, st.o[2], (int)vsw, sprev);
+  st.o[3] = mfma_mx<3, 0>(vop[3], pprev, st.o[3], (int)vsw, sprev);
 }
 
 struct AttnParams {
@@ -345,7 +399,7 @@ struct AttnParams {
 // LDS: the double-buffered K/V tiles of the main loop, reused afterwards (fused epilogue) for each
 // wave's decoded token-normalised own-block V, 32 keys x 128 columns of bf16 (exact: E4M3 values times
 // a power of two need 4 significant bits).
-constexpr int CB_NBUF = 3;  // ring: the tile being finished, the next one (its scores), the one arriving
+constexpr int CB_NBUF = 4;  // ring: the previous tile (its deferred P.V), this one, the next one, the one arriving
 constexpr int CB_LDS_BYTES = CB_NBUF * sizeof(TileSmem);
 static_assert(4 * 32 * 128 * 2 <= CB_LDS_BYTES, "the own-block V must fit the tile buffers");
 
@@ -490,10 +544,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
   }
   __syncthreads();
   if (!kLeaky) {
-    // Software pipeline: iteration it runs the softmax and P.V of tile it on scores computed one
-    // iteration earlier, with the next tile's score MFMAs interleaved. Tile it lives in ring slot
-    // it % 3; tile it + 2 is loaded during iteration it straight into the slot of tile it - 1, which
-    // no wave reads after the barrier that ended iteration it - 1.
+    // Software pipeline: iteration it runs the softmax of tile it on scores computed one iteration
+    // earlier, with the next tile's score MFMAs and the previous tile's P.V MFMAs interleaved. Tile it
+    // lives in ring slot it % 4; tile it + 2 is loaded during iteration it straight into the slot of
+    // tile it - 2, which no wave reads after the barrier that ended iteration it - 1.
     const int nfull = e_w / CB_BN;                   // full tiles of this wave
     const int nt_w = nfull + (e_w % CB_BN ? 1 : 0);  // tiles with completed keys of this wave
     v16f sa[2], sb[2];
@@ -503,22 +557,31 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
       else
         scores<false>(sa, sm[0], qop, qsc, c, hf);
     }
+    v8i pprev = {};  // the deferred P codes and this lane's E8M0 byte (zero codes before the first tile)
+    int sprev = 127;
     auto step = [&](int it, v16f(&sc)[2], v16f(&sn)[2]) {
       const int kt0 = it * CB_BN;
-      const int slot = it % CB_NBUF;
-      const int slot2 = slot == 0 ? CB_NBUF - 1 : slot - 1;  // (it + 2) % 3
+      const int slot = it % CB_NBUF, slot2 = (it + 2) % CB_NBUF, slotp = (it + CB_NBUF - 1) % CB_NBUF;
       if (it + 2 < ntiles) TILE_LOAD(sm[slot2], psc, kt0 + 2 * CB_BN);
       const TileSmem& cur = sm[slot];
-      const TileSmem& nxt = sm[slot == CB_NBUF - 1 ? 0 : slot + 1];
+      const TileSmem& nxt = sm[(it + 1) % CB_NBUF];
+      // on iteration 0 there is no previous tile: its zero codes meet tile 0's own (loaded, finite) V
+      const TileSmem& prv = sm[it == 0 ? slot : slotp];
       if (it < nfull) {
         if (it + 1 < nfull)
-          softmax_pv<true, 2>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+          softmax_pv<true, 2, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+                                        it == 0);
         else if (it + 1 < nt_w)
-          softmax_pv<true, 1>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+          softmax_pv<true, 1, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+                                        it == 0);
         else
-          softmax_pv<true, 0>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+          softmax_pv<true, 0, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+                                        it == 0);
       } else if (it < nt_w) {
-        softmax_pv<false, 0>(st, sc, cur, sn, nxt, qop, qsc, scale_log2, c, hf, it == 0);
+        softmax_pv<false, 0, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+                                       it == 0);
+      } else if (it == nt_w && nt_w > 0) {
+        pv_deferred(st, prv, pprev, sprev, c, hf);  // the P.V of the wave's last tile
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);
       if (it + 2 < ntiles) store_scales(sm[slot2], psc, tid);
@@ -529,6 +592,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
       step(it, sa, sb);
       if (it + 1 < ntiles) step(it + 1, sb, sa);
     }
+    if (nt_w == ntiles && nt_w > 0) pv_deferred(st, sm[(ntiles - 1) % CB_NBUF], pprev, sprev, c, hf);
+    __syncthreads();  // every wave's deferred LDS reads are done before the epilogue reuses the LDS
   }
   // Ordinary causal variant: the plain loop (no next-tile scores), the own block masked per element.
   for (int it = 0; kLeaky && it < ntiles; ++it) {
@@ -537,15 +602,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
     if (it + 1 < ntiles) TILE_LOAD(sm[(it + 1) & 1], psc, kt0 + CB_BN);
     const TileSmem& cur = sm[it & 1];
     v16f sacc[2], none[2];
+    v8i nop8 = {};
+    int nsc = 127;
     if (kt0 + CB_BN <= e_w) {
       scores<true>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<true>(st, sacc, cur, none, cur, qop, qsc, scale_log2, c, hf, it == 0);
+      softmax_pv<true>(st, sacc, cur, none, cur, cur, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
     } else if (kt0 < e_w) {  // completed block, then the own block (masked)
       scores<true>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<true, 0, 1>(st, sacc, cur, none, cur, qop, qsc, scale_log2, c, hf, it == 0);
+      softmax_pv<true, 0, 1>(st, sacc, cur, none, cur, cur, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
     } else if (wave_valid && kt0 == e_w) {  // the own block opens this tile (masked)
       scores<false>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<false, 0, 0>(st, sacc, cur, none, cur, qop, qsc, scale_log2, c, hf, it == 0);
+      softmax_pv<false, 0, 0>(st, sacc, cur, none, cur, cur, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
     }
     // The next tile's loads (LDS and scale word) are complete here on every path; then its scales
     // are stored and the barrier publishes the tile.
