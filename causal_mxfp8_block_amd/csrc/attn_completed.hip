@@ -45,6 +45,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace mxfa {
 
 constexpr int CB_BM = 128;    // queries per workgroup (4 waves x 32)
@@ -206,13 +208,14 @@ __device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const
 // MFMA per group of exponentials. kMaskBlk (ordinary causal variant only, with kNext = 0): that block
 // is the wave's own 32-token block, of which query qw + c sees keys qw .. qw + c; the others get
 // p = 0, and its E8M0 comes from the visible keys. kDefer: this tile's P.V is not issued here but
-// handed out in (pprev, sprev); the previous tile's, handed in the same way, is issued here, one
-// MFMA per group of exponentials, on the V of tp (zero codes, which add exactly 0, when there is
-// no previous tile). With kDefer the matrix core runs beside the VALU for all eight MFMAs of a
-// tile, and no P.V waits at the end of the softmax.
+// handed out in (pout, sout); the previous tile's, handed in as (pprev, sprev), is issued here, one
+// MFMA per group of exponentials, on the V of tp (zero codes on zero V, which add exactly 0, when
+// there is no previous tile). With kDefer the matrix core runs beside the VALU for all eight MFMAs
+// of a tile, and no P.V waits at the end of the softmax.
 template <bool kFull, int kNext = 0, int kMaskBlk = -1, bool kDefer = false>
 __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const TileSmem& t, v16f (&snext)[2],
-                                           const TileSmem& tn, const TileSmem& tp, v8i& pprev, int& sprev,
+                                           const TileSmem& tn, const TileSmem& tp, const v8i& pprev, int sprev,
+                                           v8i& pout, int& sout,
                                            const v8i (&qop)[2], const int (&qsc)[2], float scale_log2, int c,
                                            int hf, bool first) {
   static_assert(kMaskBlk < 0 || (kNext == 0 && !kDefer), "the masked own block is the wave's last tile");
@@ -328,12 +331,16 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     float q[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[0][4 * g + e], scale_log2, nb0));
-    ls0 += (q[0] + q[1]) + (q[2] + q[3]);
+    {
+      const float s4 = (q[0] + q[1]) + (q[2] + q[3]);
+      ls0 = g == 0 ? s4 : ls0 + s4;  // no add of the initial zero
+    }
     pop[g] = pack4_p(q[0], q[1], q[2], q[3]);
     if (kFull) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[1][4 * g + e], scale_log2, nb1));
-      ls1 += (q[0] + q[1]) + (q[2] + q[3]);
+      const float s4 = (q[0] + q[1]) + (q[2] + q[3]);
+      ls1 = g == 0 ? s4 : ls1 + s4;
       pop[4 + g] = pack4_p(q[0], q[1], q[2], q[3]);
     } else {
       pop[4 + g] = 0;
@@ -350,8 +357,8 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
   st.lsum += kFull ? ldexpf(ls0, e0 - 127) + ldexpf(ls1, e1 - 127) : ldexpf(ls0, e0 - 127);
   const int psc = hf ? e1 : e0;
   if (kDefer) {  // this tile's P.V goes to the next iteration
-    pprev = pop;
-    sprev = psc;
+    pout = pop;
+    sout = psc;
     return;
   }
   st.o[0] = mfma_mx<0, 0>(vop[0], pop, st.o[0], (int)vsw, psc);
@@ -542,6 +549,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     store_scales(sm[1], psc, tid);
   }
+  if (!kLeaky) {
+    // Slot 3 stands in for tile -1 in iteration 0 (the deferred P.V of no tile): zero V codes and
+    // E8M0 bytes, which add exactly 0. Tile 3 first arrives there in iteration 1.
+    uint4* z = reinterpret_cast<uint4*>(sm[CB_NBUF - 1].v);
+    for (int i = tid; i < 128 * CB_VROW / 16; i += 256) z[i] = uint4{0u, 0u, 0u, 0u};
+    if (tid < 64) reinterpret_cast<uint32_t*>(sm[CB_NBUF - 1].vs)[tid] = 0u;
+  }
   __syncthreads();
   if (!kLeaky) {
     // Software pipeline: iteration it runs the softmax of tile it on scores computed one iteration
@@ -557,42 +571,52 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
       else
         scores<false>(sa, sm[0], qop, qsc, c, hf);
     }
-    v8i pprev = {};  // the deferred P codes and this lane's E8M0 byte (zero codes before the first tile)
-    int sprev = 127;
-    auto step = [&](int it, v16f(&sc)[2], v16f(&sn)[2]) {
+    // Deferred P codes and this lane's E8M0 byte: tile j's in (pb, spb) for even j, (pa, spa) for odd j
+    // (zero codes for tile -1).
+    v8i pa = {}, pb = {};
+    int spa = 127, spb = 127;
+    // Iteration it with its ring slots known at compile time (s = it % 4): the tile it + 2 load goes
+    // to slot (s + 2) % 4, and the LDS addresses of the iteration are constants off per-lane bases.
+    auto step = [&](auto kslot, int it, v16f(&sc)[2], v16f(&sn)[2], const v8i& pin, int sin, v8i& pout, int& sout) {
+      constexpr int s = decltype(kslot)::value;
       const int kt0 = it * CB_BN;
-      const int slot = it % CB_NBUF, slot2 = (it + 2) % CB_NBUF, slotp = (it + CB_NBUF - 1) % CB_NBUF;
-      if (it + 2 < ntiles) TILE_LOAD(sm[slot2], psc, kt0 + 2 * CB_BN);
-      const TileSmem& cur = sm[slot];
-      const TileSmem& nxt = sm[(it + 1) % CB_NBUF];
-      // on iteration 0 there is no previous tile: its zero codes meet tile 0's own (loaded, finite) V
-      const TileSmem& prv = sm[it == 0 ? slot : slotp];
+      if (it + 2 < ntiles) TILE_LOAD(sm[(s + 2) % CB_NBUF], psc, kt0 + 2 * CB_BN);
+      const TileSmem& cur = sm[s];
+      const TileSmem& nxt = sm[(s + 1) % CB_NBUF];
+      const TileSmem& prv = sm[(s + CB_NBUF - 1) % CB_NBUF];
       if (it < nfull) {
         if (it + 1 < nfull)
-          softmax_pv<true, 2, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+          softmax_pv<true, 2, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
                                         it == 0);
         else if (it + 1 < nt_w)
-          softmax_pv<true, 1, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+          softmax_pv<true, 1, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
                                         it == 0);
         else
-          softmax_pv<true, 0, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+          softmax_pv<true, 0, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
                                         it == 0);
       } else if (it < nt_w) {
-        softmax_pv<false, 0, -1, true>(st, sc, cur, sn, nxt, prv, pprev, sprev, qop, qsc, scale_log2, c, hf,
+        softmax_pv<false, 0, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
                                        it == 0);
       } else if (it == nt_w && nt_w > 0) {
-        pv_deferred(st, prv, pprev, sprev, c, hf);  // the P.V of the wave's last tile
+        pv_deferred(st, prv, pin, sin, c, hf);  // the P.V of the wave's last tile
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);
-      if (it + 2 < ntiles) store_scales(sm[slot2], psc, tid);
+      if (it + 2 < ntiles) store_scales(sm[(s + 2) % CB_NBUF], psc, tid);
       __syncthreads();
     };
-    // unrolled by two so that the two score buffers swap roles without register copies
-    for (int it = 0; it < ntiles; it += 2) {
-      step(it, sa, sb);
-      if (it + 1 < ntiles) step(it + 1, sb, sa);
+    // unrolled by four: the slots are constants, and the score and P buffers swap roles without copies
+    for (int it = 0; it < ntiles; it += 4) {
+      step(std::integral_constant<int, 0>{}, it, sa, sb, pa, spa, pb, spb);
+      if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1, sb, sa, pb, spb, pa, spa);
+      if (it + 2 < ntiles) step(std::integral_constant<int, 2>{}, it + 2, sa, sb, pa, spa, pb, spb);
+      if (it + 3 < ntiles) step(std::integral_constant<int, 3>{}, it + 3, sb, sa, pb, spb, pa, spa);
     }
-    if (nt_w == ntiles && nt_w > 0) pv_deferred(st, sm[(ntiles - 1) % CB_NBUF], pprev, sprev, c, hf);
+    if (nt_w == ntiles && nt_w > 0) {
+      if ((ntiles - 1) & 1)
+        pv_deferred(st, sm[(ntiles - 1) % CB_NBUF], pa, spa, c, hf);
+      else
+        pv_deferred(st, sm[(ntiles - 1) % CB_NBUF], pb, spb, c, hf);
+    }
     __syncthreads();  // every wave's deferred LDS reads are done before the epilogue reuses the LDS
   }
   // Ordinary causal variant: the plain loop (no next-tile scores), the own block masked per element.
@@ -606,13 +630,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
     int nsc = 127;
     if (kt0 + CB_BN <= e_w) {
       scores<true>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<true>(st, sacc, cur, none, cur, cur, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
+      softmax_pv<true>(st, sacc, cur, none, cur, cur, nop8, nsc, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
     } else if (kt0 < e_w) {  // completed block, then the own block (masked)
       scores<true>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<true, 0, 1>(st, sacc, cur, none, cur, cur, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
+      softmax_pv<true, 0, 1>(st, sacc, cur, none, cur, cur, nop8, nsc, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
     } else if (wave_valid && kt0 == e_w) {  // the own block opens this tile (masked)
       scores<false>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<false, 0, 0>(st, sacc, cur, none, cur, cur, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
+      softmax_pv<false, 0, 0>(st, sacc, cur, none, cur, cur, nop8, nsc, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
     }
     // The next tile's loads (LDS and scale word) are complete here on every path; then its scales
     // are stored and the barrier publishes the tile.
