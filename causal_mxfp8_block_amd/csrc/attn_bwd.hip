@@ -194,6 +194,96 @@ struct DkdvTiles {
   uint16_t qt[128 * 32], gt[128 * 32];  // Q^T, dO^T rows (slot order): chunk c of row d in slot c ^ ((d >> 2) & 3)
   float l[32], d[32];                   // lse * log2(e) and Delta of the step's 32 queries
 };
+// Step n_'s tiles from global memory straight into slot T (lane l's bytes at the wave's base + 16 l):
+// thread tid fills LDS chunk tid (16 bytes) of each of the four tiles: of Q and dO, row r = tid/16,
+// slot tid%16, holding chunk (tid%16) ^ (r & 15) of that query's row; of Q^T and dO^T, row d = tid/4,
+// slot tid%4, holding chunk (tid%4) ^ ((d >> 2) & 3) of the block's 64 bytes of row d. Wave 0 also
+// moves the 32 lse * log2(e) and 32 Delta values (4 bytes per lane).
+__device__ __forceinline__ void dkdv_fetch(const uint16_t* __restrict__ qd, const uint16_t* __restrict__ gd,
+                                           const uint16_t* __restrict__ qdt, const uint16_t* __restrict__ gdt,
+                                           const float* __restrict__ lse2, const float* __restrict__ delta,
+                                           DkdvTiles* __restrict__ T, int n_, int b, int hk, int G, int per_head,
+                                           int nqb, int S, int Hq, int rr, int rx, int td, int tx, int lane,
+                                           int wave_u) {
+  const int hq_ = hk * G + n_ / per_head, q0_ = 32 * (nqb - 1 - n_ % per_head);
+  const int64_t bhq_ = (int64_t)b * Hq + hq_;
+  gload_lds16(qd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T->q) + 1024 * wave_u);
+  gload_lds16(gd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T->g) + 1024 * wave_u);
+  gload_lds16(qdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T->qt) + 1024 * wave_u);
+  gload_lds16(gdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T->gt) + 1024 * wave_u);
+  if (wave_u == 0) gload_lds4(lane < 32 ? lse2 + bhq_ * S + q0_ + lane : delta + bhq_ * S + q0_ + lane - 32, T->l);
+}
+
+// One step of the dK/dV loop: step st + 2's loads into slot L, the step's products on slot T. The
+// slots and the global sources are restrict pointers: L is not T, so the compiler can tell this
+// step's LDS reads from the loads in flight and does not wait for those loads before the reads.
+__device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ qd, const uint16_t* __restrict__ gd,
+                                          const uint16_t* __restrict__ qdt, const uint16_t* __restrict__ gdt,
+                                          const float* __restrict__ lse2, const float* __restrict__ delta,
+                                          const DkdvTiles* __restrict__ T, DkdvTiles* __restrict__ L, int st,
+                                          int nsteps, int b, int hk, int G, int per_head, int nqb, int S, int Hq, int rr,
+                                          int rx, int td, int tx, int lane, int wave_u, int n, int g, int key0,
+                                          float scale_log2, const v8bf (&kop)[4], const v8bf (&vop)[4], v4f (&dkT)[8],
+                                          v4f (&dvT)[8]) {
+  // step st + 2 into the slot of step st - 1, which no wave reads after the barrier that ended it
+  if (st + 2 < nsteps)
+    dkdv_fetch(qd, gd, qdt, gdt, lse2, delta, L, st + 2, b, hk, G, per_head, nqb, S, Hq, rr, rx, td, tx, lane, wave_u);
+  __builtin_amdgcn_sched_barrier(0);
+  const int qb = nqb - 1 - st % per_head;
+  {  // every wave computes every step (branch-free); key > query is masked below
+    v4f sacc[2], pacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      v8bf qa[4], ga[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int off = (16 * mt + n) * 128 + 8 * ((4 * s + g) ^ n);  // row 16mt + n: (row & 15) = n
+        qa[s] = ld8bf(T->q + off);
+        ga[s] = ld8bf(T->g + off);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[mt][i] = pacc[mt][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sacc[mt] = mfma16(qa[s], kop[s], sacc[mt]);
+        pacc[mt] = mfma16(ga[s], vop[s], pacc[mt]);
+      }
+    }
+    // P = 2^(S scale log2e - lse log2e) and dS = P (dP - Delta); query 16mt + 4g + i, key key0 + n
+    const int koff = key0 - 32 * qb;  // key - query offset of the two blocks' first tokens
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const float4 l4 = *reinterpret_cast<const float4*>(T->l + 16 * mt + 4 * g);
+      const float4 d4 = *reinterpret_cast<const float4*>(T->d + 16 * mt + 4 * g);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], scale_log2, -lv[i]));
+        if (n + koff > 16 * mt + 4 * g + i) p = 0.f;  // key after query
+        sacc[mt][i] = p;
+        pacc[mt][i] = p * (pacc[mt][i] - dv[i]);
+      }
+    }
+    v8bf pb, sb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb[e] = (__bf16)sacc[e >> 2][e & 3];
+      sb[e] = (__bf16)pacc[e >> 2][e & 3];
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS: one MFMA per 16-row tile of D (K = the 32 queries)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int off = (16 * dt + n) * 32 + 8 * (g ^ ((n >> 2) & 3));  // row 16dt + n
+      dvT[dt] = mfma16(ld8bf(T->gt + off), pb, dvT[dt]);
+      dkT[dt] = mfma16(ld8bf(T->qt + off), sb, dkT[dt]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // The loads issued at the top of this step (step st + 2) complete here; the barrier publishes them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(const BwdParams P) {
   __shared__ __align__(16) DkdvTiles buf[DKDV_NBUF];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
@@ -217,84 +307,19 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
   const int nqb = S / 32, qb0 = 4 * kt, per_head = nqb - qb0, nsteps = G * per_head;
-  // Thread tid fills LDS chunk tid (16 bytes) of each of the four tiles: of Q and dO, row r = tid/16,
-  // slot tid%16, holding chunk (tid%16) ^ (r & 15) of that query's row; of Q^T and dO^T, row
-  // d = tid/4, slot tid%4, holding chunk (tid%4) ^ ((d >> 2) & 3) of the block's 64 bytes of row d.
-  // Wave 0 also moves the 32 lse * log2(e) and 32 Delta values (4 bytes per lane).
+  // this thread's LDS chunk of the tiles (row and source chunk; the fetch below)
   const int rr = tid >> 4, rx = (tid & 15) ^ (rr & 15), td = tid >> 2, tx = (tid & 3) ^ ((td >> 2) & 3);
-  auto fetch = [&](int n_, DkdvTiles& T) {
-    const int hq_ = hk * G + n_ / per_head, q0_ = 32 * (nqb - 1 - n_ % per_head);
-    const int64_t bhq_ = (int64_t)b * P.Hq + hq_;
-    gload_lds16(P.qd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T.q) + 1024 * wave_u);
-    gload_lds16(P.gd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T.g) + 1024 * wave_u);
-    gload_lds16(P.qdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T.qt) + 1024 * wave_u);
-    gload_lds16(P.gdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T.gt) + 1024 * wave_u);
-    if (wave_u == 0)
-      gload_lds4(lane < 32 ? P.lse2 + bhq_ * S + q0_ + lane : P.delta + bhq_ * S + q0_ + lane - 32, T.l);
-  };
-  fetch(0, buf[0]);
-  if (nsteps > 1) fetch(1, buf[1]);
+  dkdv_fetch(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[0], 0, b, hk, G, per_head, nqb, S, P.Hq, rr, rx, td, tx,
+             lane, wave_u);
+  if (nsteps > 1)
+    dkdv_fetch(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[1], 1, b, hk, G, per_head, nqb, S, P.Hq, rr, rx, td, tx,
+               lane, wave_u);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    // step st + 2 into the slot of step st - 1, which no wave reads after the barrier that ended it
-    if (st + 2 < nsteps) fetch(st + 2, buf[(st + 2) % DKDV_NBUF]);
-    __builtin_amdgcn_sched_barrier(0);
-    const DkdvTiles& T = buf[st % DKDV_NBUF];
-    const int qb = nqb - 1 - st % per_head;
-    {  // every wave computes every step (branch-free); key > query is masked below
-      v4f sacc[2], pacc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        v8bf qa[4], ga[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int off = (16 * mt + n) * 128 + 8 * ((4 * s + g) ^ n);  // row 16mt + n: (row & 15) = n
-          qa[s] = ld8bf(T.q + off);
-          ga[s] = ld8bf(T.g + off);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[mt][i] = pacc[mt][i] = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          sacc[mt] = mfma16(qa[s], kop[s], sacc[mt]);
-          pacc[mt] = mfma16(ga[s], vop[s], pacc[mt]);
-        }
-      }
-      // P = 2^(S scale log2e - lse log2e) and dS = P (dP - Delta); query 16mt + 4g + i, key key0 + n
-      const int koff = key0 - 32 * qb;  // key - query offset of the two blocks' first tokens
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const float4 l4 = *reinterpret_cast<const float4*>(T.l + 16 * mt + 4 * g);
-        const float4 d4 = *reinterpret_cast<const float4*>(T.d + 16 * mt + 4 * g);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], P.scale_log2, -lv[i]));
-          if (n + koff > 16 * mt + 4 * g + i) p = 0.f;  // key after query
-          sacc[mt][i] = p;
-          pacc[mt][i] = p * (pacc[mt][i] - dv[i]);
-        }
-      }
-      v8bf pb, sb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = (__bf16)sacc[e >> 2][e & 3];
-        sb[e] = (__bf16)pacc[e >> 2][e & 3];
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS: one MFMA per 16-row tile of D (K = the 32 queries)
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int off = (16 * dt + n) * 32 + 8 * (g ^ ((n >> 2) & 3));  // row 16dt + n
-        dvT[dt] = mfma16(ld8bf(T.gt + off), pb, dvT[dt]);
-        dkT[dt] = mfma16(ld8bf(T.qt + off), sb, dkT[dt]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // The loads issued at the top of this step (step st + 2) complete here; the barrier publishes them.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  }
+  for (int st = 0; st < nsteps; ++st)
+    dkdv_step(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[st % DKDV_NBUF],
+              &buf[(st + 2) % DKDV_NBUF], st, nsteps, b, hk, G, per_head, nqb, S, P.Hq, rr, rx, td, tx, lane, wave_u,
+              n, g, key0, P.scale_log2, kop, vop, dkT, dvT);
   if (!valid) return;
   // lane (key n, g), element i of tile dt: column 16dt + 4g + i
   const int64_t off = b * P.ksb + (int64_t)(key0 + n) * P.kss + hk * P.ksh + 4 * g;
