@@ -31,6 +31,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace mxfa {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -186,8 +188,10 @@ __device__ __forceinline__ void gload_lds4(const void* g, void* lds) {
 // P and dS as the B operand straight from those accumulators (element i of row tile mt is query
 // 16mt + 4g + i: slot (g, e) of the contraction is query 16(e/4) + 4g + e%4, the order in which the
 // preparation pass stores the transposed copies). Each step's tiles go from global memory straight
-// into a ring of three LDS slots (loads with the LDS flag, no registers), two steps ahead.
-constexpr int DKDV_NBUF = 3;  // LDS ring: the step computing, the previous one (free), the one arriving
+// into a ring of four LDS slots (loads with the LDS flag, no registers), two steps ahead. The loop is
+// software-pipelined: while the VALU computes P and dS of step st, the matrix core runs the S and dP
+// products of step st + 1 and the dV and dK products of step st - 1.
+constexpr int DKDV_NBUF = 4;  // LDS ring: steps st - 1, st, st + 1 and st + 2 (arriving)
 struct DkdvTiles {
   // Unpadded rows; reads stay conflict-free through XOR swizzles of the 16-byte chunks:
   uint16_t q[32 * 128], g[32 * 128];    // Q, dO rows: chunk c of row r in slot c ^ (r & 15)
@@ -214,72 +218,72 @@ __device__ __forceinline__ void dkdv_fetch(const uint16_t* __restrict__ qd, cons
   if (wave_u == 0) gload_lds4(lane < 32 ? lse2 + bhq_ * S + q0_ + lane : delta + bhq_ * S + q0_ + lane - 32, T->l);
 }
 
-// One step of the dK/dV loop: step st + 2's loads into slot L, the step's products on slot T. The
-// slots and the global sources are restrict pointers: L is not T, so the compiler can tell this
-// step's LDS reads from the loads in flight and does not wait for those loads before the reads.
-__device__ __forceinline__ void dkdv_step(const uint16_t* __restrict__ qd, const uint16_t* __restrict__ gd,
-                                          const uint16_t* __restrict__ qdt, const uint16_t* __restrict__ gdt,
-                                          const float* __restrict__ lse2, const float* __restrict__ delta,
-                                          const DkdvTiles* __restrict__ T, DkdvTiles* __restrict__ L, int st,
-                                          int nsteps, int b, int hk, int G, int per_head, int nqb, int S, int Hq, int rr,
-                                          int rx, int td, int tx, int lane, int wave_u, int n, int g, int key0,
-                                          float scale_log2, const v8bf (&kop)[4], const v8bf (&vop)[4], v4f (&dkT)[8],
-                                          v4f (&dvT)[8]) {
-  // step st + 2 into the slot of step st - 1, which no wave reads after the barrier that ended it
+// One iteration of the pipelined dK/dV loop: step st + 2's loads into slot L; the S and dP MFMAs of
+// step st + 1 (tiles Tn, into sn, pn) and the dV and dK MFMAs of step st - 1 (tiles Tp, with its P
+// and dS in pbp, sbp), one of each per group, interleaved with P and dS of step st (scores in sc, pc;
+// lse and Delta from Tc). The slots and the global sources are restrict pointers: L is none of Tc,
+// Tn, Tp, so the compiler can tell the LDS reads from the loads in flight and does not wait for
+// those loads before the reads. Past the last step Tn is a stale slot (its products are unused).
+__device__ __forceinline__ void dkdv_pipe_iter(
+    const uint16_t* __restrict__ qd, const uint16_t* __restrict__ gd, const uint16_t* __restrict__ qdt,
+    const uint16_t* __restrict__ gdt, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const DkdvTiles* __restrict__ Tc, const DkdvTiles* __restrict__ Tn, const DkdvTiles* __restrict__ Tp,
+    DkdvTiles* __restrict__ L, int st, int nsteps, int b, int hk, int G, int per_head, int nqb, int S, int Hq, int rr,
+    int rx, int td, int tx, int lane, int wave_u, int n, int g, int key0, float scale_log2, const v8bf (&kop)[4],
+    const v8bf (&vop)[4], v4f (&dkT)[8], v4f (&dvT)[8], v4f (&sc)[2], v4f (&pc)[2], v4f (&sn)[2], v4f (&pn)[2],
+    v8bf& pbp, v8bf& sbp) {
   if (st + 2 < nsteps)
     dkdv_fetch(qd, gd, qdt, gdt, lse2, delta, L, st + 2, b, hk, G, per_head, nqb, S, Hq, rr, rx, td, tx, lane, wave_u);
-  __builtin_amdgcn_sched_barrier(0);
   const int qb = nqb - 1 - st % per_head;
-  {  // every wave computes every step (branch-free); key > query is masked below
-    v4f sacc[2], pacc[2];
+  const int koff = key0 - 32 * qb;  // key - query offset of the two blocks' first tokens
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      v8bf qa[4], ga[4];
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int off = (16 * mt + n) * 128 + 8 * ((4 * s + g) ^ n);  // row 16mt + n: (row & 15) = n
-        qa[s] = ld8bf(T->q + off);
-        ga[s] = ld8bf(T->g + off);
-      }
+    for (int i = 0; i < 4; ++i) sn[mt][i] = pn[mt][i] = 0.f;
+  float lv[8], dv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[mt][i] = pacc[mt][i] = 0.f;
+  for (int mt = 0; mt < 2; ++mt) {
+    const float4 l4 = *reinterpret_cast<const float4*>(Tc->l + 16 * mt + 4 * g);
+    const float4 d4 = *reinterpret_cast<const float4*>(Tc->d + 16 * mt + 4 * g);
+    lv[4 * mt] = l4.x; lv[4 * mt + 1] = l4.y; lv[4 * mt + 2] = l4.z; lv[4 * mt + 3] = l4.w;
+    dv[4 * mt] = d4.x; dv[4 * mt + 1] = d4.y; dv[4 * mt + 2] = d4.z; dv[4 * mt + 3] = d4.w;
+  }
+  // operands of group k: rows 16(k/4) + n of Q and dO (step k%4 over D), row 16k + n of the transposes
+  auto rowoff = [&](int k) { return (16 * (k >> 2) + n) * 128 + 8 * ((4 * (k & 3) + g) ^ n); };
+  const int troff = n * 32 + 8 * (g ^ ((n >> 2) & 3));
+  v8bf qa = ld8bf(Tn->q + rowoff(0)), ga = ld8bf(Tn->g + rowoff(0));
+  v8bf gta = ld8bf(Tp->gt + troff), qta = ld8bf(Tp->qt + troff);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        sacc[mt] = mfma16(qa[s], kop[s], sacc[mt]);
-        pacc[mt] = mfma16(ga[s], vop[s], pacc[mt]);
-      }
+  for (int k = 0; k < 8; ++k) {
+    v8bf qa2, ga2, gta2, qta2;
+    if (k < 7) {  // the next group's operands, read one group ahead
+      qa2 = ld8bf(Tn->q + rowoff(k + 1));
+      ga2 = ld8bf(Tn->g + rowoff(k + 1));
+      gta2 = ld8bf(Tp->gt + 16 * 32 * (k + 1) + troff);
+      qta2 = ld8bf(Tp->qt + 16 * 32 * (k + 1) + troff);
     }
-    // P = 2^(S scale log2e - lse log2e) and dS = P (dP - Delta); query 16mt + 4g + i, key key0 + n
-    const int koff = key0 - 32 * qb;  // key - query offset of the two blocks' first tokens
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const float4 l4 = *reinterpret_cast<const float4*>(T->l + 16 * mt + 4 * g);
-      const float4 d4 = *reinterpret_cast<const float4*>(T->d + 16 * mt + 4 * g);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], scale_log2, -lv[i]));
-        if (n + koff > 16 * mt + 4 * g + i) p = 0.f;  // key after query
-        sacc[mt][i] = p;
-        pacc[mt][i] = p * (pacc[mt][i] - dv[i]);
-      }
+    const int mt = k >> 2, s4 = k & 3;
+    sn[mt] = mfma16(qa, kop[s4], sn[mt]);
+    pn[mt] = mfma16(ga, vop[s4], pn[mt]);
+    dvT[k] = mfma16(gta, pbp, dvT[k]);
+    dkT[k] = mfma16(qta, sbp, dkT[k]);
+    {  // P and dS of element (mt, i) = (k/4, k%4) of step st; query 16mt + 4g + i, key key0 + n
+      const int i = k & 3;
+      float p = __builtin_amdgcn_exp2f(fmaf(sc[mt][i], scale_log2, -lv[k]));
+      if (n + koff > 16 * mt + 4 * g + i) p = 0.f;  // key after query
+      sc[mt][i] = p;
+      pc[mt][i] = p * (pc[mt][i] - dv[k]);
     }
-    v8bf pb, sb;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pb[e] = (__bf16)sacc[e >> 2][e & 3];
-      sb[e] = (__bf16)pacc[e >> 2][e & 3];
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS: one MFMA per 16-row tile of D (K = the 32 queries)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int off = (16 * dt + n) * 32 + 8 * (g ^ ((n >> 2) & 3));  // row 16dt + n
-      dvT[dt] = mfma16(ld8bf(T->gt + off), pb, dvT[dt]);
-      dkT[dt] = mfma16(ld8bf(T->qt + off), sb, dkT[dt]);
+    if (k < 7) {
+      qa = qa2; ga = ga2; gta = gta2; qta = qta2;
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
-  // The loads issued at the top of this step (step st + 2) complete here; the barrier publishes them.
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {  // slot (g, e) of the next dV/dK products: query 16(e/4) + 4g + e%4
+    pbp[e] = (__bf16)sc[e >> 2][e & 3];
+    sbp[e] = (__bf16)pc[e >> 2][e & 3];
+  }
+  // The loads issued at the top of this iteration (step st + 2) complete here; the barrier publishes them.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 }
@@ -309,6 +313,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int nqb = S / 32, qb0 = 4 * kt, per_head = nqb - qb0, nsteps = G * per_head;
   // this thread's LDS chunk of the tiles (row and source chunk; the fetch below)
   const int rr = tid >> 4, rx = (tid & 15) ^ (rr & 15), td = tid >> 2, tx = (tid & 3) ^ ((td >> 2) & 3);
+  // Slot 3 stands in for step -1 in iteration 0: zero transposed tiles, which with zero P and dS add
+  // exactly 0. Step 3 first arrives there in iteration 1.
+  {
+    uint4* z0 = reinterpret_cast<uint4*>(buf[DKDV_NBUF - 1].qt);
+    uint4* z1 = reinterpret_cast<uint4*>(buf[DKDV_NBUF - 1].gt);
+    z0[tid] = uint4{0u, 0u, 0u, 0u};
+    z1[tid] = uint4{0u, 0u, 0u, 0u};
+  }
   dkdv_fetch(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[0], 0, b, hk, G, per_head, nqb, S, P.Hq, rr, rx, td, tx,
              lane, wave_u);
   if (nsteps > 1)
@@ -316,10 +328,45 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                lane, wave_u);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st)
-    dkdv_step(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[st % DKDV_NBUF],
-              &buf[(st + 2) % DKDV_NBUF], st, nsteps, b, hk, G, per_head, nqb, S, P.Hq, rr, rx, td, tx, lane, wave_u,
-              n, g, key0, P.scale_log2, kop, vop, dkT, dvT);
+  // S and dP of step 0
+  v4f sa[2], pa[2], sb[2], pb2[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[mt][i] = pa[mt][i] = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int off = (16 * mt + n) * 128 + 8 * ((4 * s4 + g) ^ n);
+      sa[mt] = mfma16(ld8bf(buf[0].q + off), kop[s4], sa[mt]);
+      pa[mt] = mfma16(ld8bf(buf[0].g + off), vop[s4], pa[mt]);
+    }
+  }
+  v8bf pbp, sbp;  // P and dS of the previous step (none before step 0)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pbp[e] = sbp[e] = (__bf16)0.f;
+  // unrolled by four: ring slots are constants (step st in slot st % 4); S and dP buffers alternate
+  auto it4 = [&](auto kslot, int st, v4f (&sc)[2], v4f (&pc)[2], v4f (&sn)[2], v4f (&pn)[2]) {
+    constexpr int s = decltype(kslot)::value;
+    dkdv_pipe_iter(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[s], &buf[(s + 1) % DKDV_NBUF],
+                   &buf[(s + 3) % DKDV_NBUF], &buf[(s + 2) % DKDV_NBUF], st, nsteps, b, hk, G, per_head, nqb, S, P.Hq,
+                   rr, rx, td, tx, lane, wave_u, n, g, key0, P.scale_log2, kop, vop, dkT, dvT, sc, pc, sn, pn, pbp,
+                   sbp);
+  };
+  for (int st = 0; st < nsteps; st += 4) {
+    it4(std::integral_constant<int, 0>{}, st, sa, pa, sb, pb2);
+    if (st + 1 < nsteps) it4(std::integral_constant<int, 1>{}, st + 1, sb, pb2, sa, pa);
+    if (st + 2 < nsteps) it4(std::integral_constant<int, 2>{}, st + 2, sa, pa, sb, pb2);
+    if (st + 3 < nsteps) it4(std::integral_constant<int, 3>{}, st + 3, sb, pb2, sa, pa);
+  }
+  {  // dV and dK of the last step
+    const DkdvTiles& Tp = buf[(nsteps - 1) % DKDV_NBUF];
+    const int troff = n * 32 + 8 * (g ^ ((n >> 2) & 3));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      dvT[k] = mfma16(ld8bf(Tp.gt + 16 * 32 * k + troff), pbp, dvT[k]);
+      dkT[k] = mfma16(ld8bf(Tp.qt + 16 * 32 * k + troff), sbp, dkT[k]);
+    }
+  }
   if (!valid) return;
   // lane (key n, g), element i of tile dt: column 16dt + 4g + i
   const int64_t off = b * P.ksb + (int64_t)(key0 + n) * P.kss + hk * P.ksh + 4 * g;
