@@ -11,13 +11,13 @@
 //  * A preparation pass decodes Q, K and V to bf16 (exact: an E4M3 value times a power of two has 4
 //    significant bits) and copies dO, each head-major, plus a transposed [D][S] copy of Q, K and dO
 //    for the MFMA operands that contract over tokens; it also forms Delta.
-//  * dK/dV kernel: one wave per 32 keys, their K and V operands held in registers. For every query
-//    head of the KV head and every 32-query block at or after the keys, it computes S = Q K^T and
-//    dP = dO V^T (keys on the lanes, queries on the accumulator elements), P and dS elementwise, and
-//    accumulates dV^T += dO^T P and dK^T += Q^T dS. P and dS stay in their accumulator registers and
-//    are the B operand of those MFMAs: the accumulator's query order is a permutation of the B
-//    operand's contraction order, and the A operand (dO^T, Q^T, read from LDS) is read in the same
-//    permuted order.
+//  * dK/dV kernel: one wave per 16 keys, two waves per SIMD, their K and V operands held in registers
+//    (16x16x32 MFMAs). For every query head of the KV head and every 32-query block at or after the
+//    keys, it computes S = Q K^T and dP = dO V^T (keys on the lanes, queries on the accumulator
+//    elements), P and dS elementwise, and accumulates dV^T += dO^T P and dK^T += Q^T dS. P and dS stay
+//    in their accumulator registers and are the B operand of those MFMAs: the accumulator's query
+//    order is a permutation of the B operand's contraction order, and the A operand (dO^T, Q^T, read
+//    from LDS) is read in the same permuted order. The steps are software-pipelined.
 //  * dQ kernel: one wave per 32 queries, their Q and dO operands in registers. For every 32-key block
 //    at or before the queries it computes S^T = K Q^T and dP^T = V dO^T (queries on the lanes: lse and
 //    Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way.
