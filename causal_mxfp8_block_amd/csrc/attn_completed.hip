@@ -113,15 +113,12 @@ __device__ __forceinline__ void swap32f(float& x, float& y) {
   y = __builtin_bit_cast(float, b);
 }
 
-// One thread's share of a tile load, through buffer resources over the current (b, kv-head) slice:
-// two 16-byte K chunks (key row tid/4 at byte offset kvoff), two 16-byte V chunks (column tid/2 at
-// byte offset vvoff) and, in waves 0 and 1, one scale word: wave 0 the 4 E8M0 bytes of key tid, wave
-// 1 one word of the tile's two V scale blocks. The per-tile offset is a scalar.
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-// Thread tid fills LDS chunks c = 256 i + tid (i = 0, 1) of the K tile (row c/8, slot c%8) and of the
-// V tile (column c/4, slot c%4); the wave's 64 chunks of one instruction are contiguous.
+// One thread's share of a tile load, through buffer resources over the current (b, kv-head) slice,
+// straight into LDS: thread tid fills LDS chunks c = 256 i + tid (i = 0, 1) of the K tile (row c/8,
+// slot c%8, from byte offset kvoff) and of the V tile (column c/4, slot c%4, from byte offset vvoff);
+// the wave's 64 chunks of one instruction are contiguous. In waves 0 and 1 it also loads one scale
+// word into sc: wave 0 the 4 E8M0 bytes of key tid, wave 1 one word of the tile's two V scale blocks.
+// The per-tile offset is a scalar.
 #define TILE_LOAD(T, sc, kt0)                                                                    \
   do {                                                                                           \
     bload_lds16(rk, (T).k + 16 * (64 * wave_u), kvoff0, (kt0) * 128);                            \
