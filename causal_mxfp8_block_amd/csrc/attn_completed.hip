@@ -26,15 +26,14 @@
 //    the block-scaled FP8 MFMA again, on the columnwise V codes (keys contiguous per column).
 //  * O^T leaves one query per lane too, so the rescale and the final 1/l are per-lane scalars.
 //  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the LDS flag), once per
-//    workgroup, shared by the 4 waves: a ring of four tiles, one barrier per tile. No register holds
-//    a tile in flight.
-//  * Software pipeline: while a wave runs the softmax of tile n, it issues the four score MFMAs of
-//    tile n + 1 and the four P.V MFMAs of tile n - 1, one of each per group of exponentials, so the
-//    matrix core works beside the VALU within the wave; tile n + 2 arrives meanwhile. A deferred P
-//    block stays exact across a rescale: its E8M0 byte drops by the same power of two. The ordinary
-//    causal variant keeps a plain loop.
-//  * Two workgroups per CU (two waves per SIMD, up to 254 VGPRs each): the softmax VALU work of one
-//    wave also overlaps the MFMAs and memory waits of the other.
+//    workgroup, shared by the 4 waves: double-buffered, one barrier per tile. No register holds a
+//    tile in flight. A tile's loads are issued after the score MFMAs of the previous tile, so the
+//    wait for them falls after that tile's softmax.
+//  * Three workgroups per CU (three waves per SIMD, at most 168 VGPRs each): one wave's softmax VALU
+//    work overlaps the MFMAs, LDS reads and barrier waits of the other two. Within a wave the loop is
+//    plain (scores, softmax, P.V), with the V operands read next to their MFMAs so that few
+//    registers live across the softmax; a software-pipelined loop that overlaps MFMA and VALU within
+//    one wave needs 255 VGPRs, allows only two waves per SIMD, and is slower.
 //  * Full tiles and the half tile at the end of a wave's range are separate code paths, so the
 //    common path has no per-element select.
 //  * One-dimensional grid in global longest-first order: all (batch, head) pairs of the last query
@@ -45,7 +44,6 @@
 #include "device_common.h"
 #include "launch.h"
 
-#include <type_traits>
 
 namespace mxfa {
 
@@ -197,81 +195,21 @@ __device__ __forceinline__ void scores(v16f (&sacc)[2], const TileSmem& t, const
   for (int kt = 0; kt < nkt; ++kt) sacc[kt] = mfma_mx<1, 0>(kop[kt][1], qop[1], sacc[kt], ksc[kt], qsc[1]);
 }
 
-// Softmax, P quantisation and O^T += V^T P^T for one tile whose scores are in sacc, with the score
-// MFMAs of the next tile (in tn, into snext) interleaved. kFull: both 32-key blocks are visible keys of
-// this wave; otherwise only the first one is (the second one's p is zero). kNext: the next tile's
-// scores to compute, 2 both of its blocks, 1 its first block, 0 none. They depend on nothing this
-// softmax computes, so the matrix core works on them while this wave's VALU runs the softmax: one
-// MFMA per group of exponentials. kMaskBlk (ordinary causal variant only, with kNext = 0): that block
-// is the wave's own 32-token block, of which query qw + c sees keys qw .. qw + c; the others get
-// p = 0, and its E8M0 comes from the visible keys. kDefer: this tile's P.V is not issued here but
-// handed out in (pout, sout); the previous tile's, handed in as (pprev, sprev), is issued here, one
-// MFMA per group of exponentials, on the V of tp (zero codes on zero V, which add exactly 0, when
-// there is no previous tile). With kDefer the matrix core runs beside the VALU for all eight MFMAs
-// of a tile, and no P.V waits at the end of the softmax.
-template <bool kFull, int kNext = 0, int kMaskBlk = -1, bool kDefer = false>
-__device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const TileSmem& t, v16f (&snext)[2],
-                                           const TileSmem& tn, const TileSmem& tp, const v8i& pprev, int sprev,
-                                           v8i& pout, int& sout,
-                                           const v8i (&qop)[2], const int (&qsc)[2], float scale_log2, int c,
+// Softmax, P quantisation and O^T += V^T P^T for one tile whose scores are in sacc. kFull: both 32-key
+// blocks are visible keys of this wave; otherwise only the first one is (the second one's p is zero).
+// kMaskBlk (ordinary causal variant only): that block is the wave's own 32-token block, of which query
+// qw + c sees keys qw .. qw + c; the others get p = 0, and its E8M0 comes from the visible keys. The V
+// operands are read from LDS just before their MFMAs, at the end: the fewest registers live across
+// the softmax, which lets three waves share a SIMD.
+template <bool kFull, int kMaskBlk = -1>
+__device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const TileSmem& t, float scale_log2, int c,
                                            int hf, bool first) {
-  static_assert(kMaskBlk < 0 || (kNext == 0 && !kDefer), "the masked own block is the wave's last tile");
-  constexpr int nmf = 2 * kNext;  // score MFMAs of the next tile: (kt, m) = (0,0), (1,0), (0,1), (1,1)
   // Lane (c, hf), element i of block kt holds key 32kt + 16hf + i of the tile, query c.
   if (kMaskBlk >= 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (16 * hf + i > c) sacc[kMaskBlk][i] = -INFINITY;
   }
-  // Next tile's K operand of MFMA j, read one group before it is used.
-  auto kread = [&](int j) {
-    const int kt = kNext == 2 ? (j & 1) : 0, m = kNext == 2 ? (j >> 1) : j;
-    const int r = 32 * kt + c;
-    const uint8_t* kr = tn.k + r * CB_KROW;
-    return make_v8i(*reinterpret_cast<const uint4*>(kr + 16 * k_slot(r, 4 * m + hf)),
-                    *reinterpret_cast<const uint4*>(kr + 16 * k_slot(r, 4 * m + 2 + hf)));
-  };
-  int ksc[2];
-  if (nmf > 0) {
-#pragma unroll
-    for (int kt = 0; kt < kNext; ++kt)
-      ksc[kt] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(tn.ks) + (32 * kt + c) * 4 + 2 * hf);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) snext[kt][i] = 0.f;
-  }
-  v8i kcur = nmf > 0 ? kread(0) : v8i{};
-  // This tile's V^T operands: lane (c, hf), tile dt: column 32dt + c, keys 16hf + [0,16) and
-  // 32 + 16hf + [0,16). Read here when no next-tile scores are due (their latency hides under the
-  // softmax), else in the last group, once the K operands are consumed (register pressure).
-  // With kDefer, the V^T operand of the previous tile's P.V MFMA dt, read one group before its use.
-  v8i vop[4];
-  uint32_t vsw;
-  auto vread = [&]() {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = 32 * dt + c;
-      const uint8_t* vr = t.v + d * CB_VROW;
-      vop[dt] = make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
-                         *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
-    }
-    vsw = *reinterpret_cast<const uint32_t*>(t.vs + hf * 128 + c * 4);
-  };
-  auto vread_prev = [&](int dt) {
-    const int d = 32 * dt + c;
-    const uint8_t* vr = tp.v + d * CB_VROW;
-    return make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
-                    *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
-  };
-  v8i vcur{};
-  if (kDefer) {
-    vsw = *reinterpret_cast<const uint32_t*>(tp.vs + hf * 128 + c * 4);
-    vcur = vread_prev(0);
-  } else if (nmf == 0) {
-    vread();
-  }
-
   float m0 = sacc[0][0], m1 = kFull ? sacc[1][0] : -INFINITY;
 #pragma unroll
   for (int i = 1; i < 16; ++i) {
@@ -293,8 +231,6 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
       for (int i = 0; i < 16; ++i) st.o[dt][i] *= f;
     st.lsum *= f;
     st.T += shift;
-    // a deferred P block was coded against the old T: its E8M0 byte drops by the same shift
-    if (kDefer) sprev = max(sprev - (int)shift, 1);
     negT = -st.T;
     pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
     pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
@@ -308,23 +244,6 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    v8i knext{};
-    if (g < nmf) {
-      const int kt = kNext == 2 ? (g & 1) : 0, m = kNext == 2 ? (g >> 1) : g;
-      snext[kt] = m == 0 ? mfma_mx<0, 0>(kcur, qop[0], snext[kt], ksc[kt], qsc[0])
-                         : mfma_mx<1, 0>(kcur, qop[1], snext[kt], ksc[kt], qsc[1]);
-      if (g + 1 < nmf) knext = kread(g + 1);
-    }
-    if (kDefer) {  // P.V MFMA g of the previous tile
-      const v8i vnx = g < 3 ? vread_prev(g + 1) : v8i{};
-      if (g == 0) st.o[0] = mfma_mx<0, 0>(vcur, pprev, st.o[0], (int)vsw, sprev);
-      if (g == 1) st.o[1] = mfma_mx<1, 0>(vcur, pprev, st.o[1], (int)vsw, sprev);
-      if (g == 2) st.o[2] = mfma_mx<2, 0>(vcur, pprev, st.o[2], (int)vsw, sprev);
-      if (g == 3) st.o[3] = mfma_mx<3, 0>(vcur, pprev, st.o[3], (int)vsw, sprev);
-      vcur = vnx;
-    } else if (nmf > 0 && g == 3) {
-      vread();
-    }
     float q[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_exp2f(fmaf(sacc[0][4 * g + e], scale_log2, nb0));
@@ -342,44 +261,22 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     } else {
       pop[4 + g] = 0;
     }
-    if (g + 1 < nmf) {
-      // order: this group's codes are complete here, and the next MFMA's operand is used only after
-      int a = pop[g], b2 = pop[4 + g];
-      asm("" : "+v"(a), "+v"(b2), "+v"(knext));
-      pop[g] = a;
-      pop[4 + g] = b2;
-      kcur = knext;
-    }
   }
   st.lsum += kFull ? ldexpf(ls0, e0 - 127) + ldexpf(ls1, e1 - 127) : ldexpf(ls0, e0 - 127);
   const int psc = hf ? e1 : e0;
-  if (kDefer) {  // this tile's P.V goes to the next iteration
-    pout = pop;
-    sout = psc;
-    return;
-  }
-  st.o[0] = mfma_mx<0, 0>(vop[0], pop, st.o[0], (int)vsw, psc);
-  st.o[1] = mfma_mx<1, 0>(vop[1], pop, st.o[1], (int)vsw, psc);
-  st.o[2] = mfma_mx<2, 0>(vop[2], pop, st.o[2], (int)vsw, psc);
-  st.o[3] = mfma_mx<3, 0>(vop[3], pop, st.o[3], (int)vsw, psc);
-}
-
-// A deferred P.V (the last one of a wave), on the V of tile tp.
-__device__ __forceinline__ void pv_deferred(RowState& st, const TileSmem& tp, const v8i& pprev, int sprev, int c,
-                                            int hf) {
-  const uint32_t vsw = *reinterpret_cast<const uint32_t*>(tp.vs + hf * 128 + c * 4);
-  v8i vop[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  // This tile's V^T operand of d-tile dt: lane (c, hf) supplies column 32dt + c, keys 16hf + [0,16) and
+  // 32 + 16hf + [0,16); its scales are byte dt of the word of column c.
+  const uint32_t vsw = *reinterpret_cast<const uint32_t*>(t.vs + hf * 128 + c * 4);
+  auto vop = [&](int dt) {
     const int d = 32 * dt + c;
-    const uint8_t* vr = tp.v + d * CB_VROW;
-    vop[dt] = make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
-                       *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
-  }
-  st.o[0] = mfma_mx<0, 0>(vop[0], pprev, st.o[0], (int)vsw, sprev);
-  st.o[1] = mfma_mx<1, 0>(vop[1], pprev, st.o[1], (int)vsw, sprev);
-  st.o[2] = mfma_mx<2, 0>(vop[2], pprev, st.o[2], (int)vsw, sprev);
-  st.o[3] = mfma_mx<3, 0>(vop[3], pprev, st.o[3], (int)vsw, sprev);
+    const uint8_t* vr = t.v + d * CB_VROW;
+    return make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
+                    *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
+  };
+  st.o[0] = mfma_mx<0, 0>(vop(0), pop, st.o[0], (int)vsw, psc);
+  st.o[1] = mfma_mx<1, 0>(vop(1), pop, st.o[1], (int)vsw, psc);
+  st.o[2] = mfma_mx<2, 0>(vop(2), pop, st.o[2], (int)vsw, psc);
+  st.o[3] = mfma_mx<3, 0>(vop(3), pop, st.o[3], (int)vsw, psc);
 }
 
 struct AttnParams {
@@ -403,7 +300,7 @@ struct AttnParams {
 // LDS: the double-buffered K/V tiles of the main loop, reused afterwards (fused epilogue) for each
 // wave's decoded token-normalised own-block V, 32 keys x 128 columns of bf16 (exact: E4M3 values times
 // a power of two need 4 significant bits).
-constexpr int CB_NBUF = 4;  // ring: the previous tile (its deferred P.V), this one, the next one, the one arriving
+constexpr int CB_NBUF = 2;  // this tile, the next one arriving
 constexpr int CB_LDS_BYTES = CB_NBUF * sizeof(TileSmem);
 static_assert(4 * 32 * 128 * 2 <= CB_LDS_BYTES, "the own-block V must fit the tile buffers");
 
@@ -415,7 +312,7 @@ static_assert(4 * 32 * 128 * 2 <= CB_LDS_BYTES, "the own-block V must fit the ti
 // "MXFP8" column under Performance), written in the output's layout.
 enum : int { MODE_COMPLETED = 0, MODE_FUSED = 1, MODE_LEAKY = 2 };
 template <int kMode>
-__global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
+__global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
   constexpr bool kFused = kMode == MODE_FUSED, kLeaky = kMode == MODE_LEAKY;
   __shared__ __align__(16) uint8_t lds[CB_LDS_BYTES];
   TileSmem* sm = reinterpret_cast<TileSmem*>(lds);  // sm[0], sm[1]
@@ -541,100 +438,36 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams P) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     store_scales(sm[0], psc, tid);
   }
-  if (!kLeaky && ntiles > 1) {
-    TILE_LOAD(sm[1], psc, CB_BN);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    store_scales(sm[1], psc, tid);
-  }
-  if (!kLeaky) {
-    // Slot 3 stands in for tile -1 in iteration 0 (the deferred P.V of no tile): zero V codes and
-    // E8M0 bytes, which add exactly 0. Tile 3 first arrives there in iteration 1.
-    uint4* z = reinterpret_cast<uint4*>(sm[CB_NBUF - 1].v);
-    for (int i = tid; i < 128 * CB_VROW / 16; i += 256) z[i] = uint4{0u, 0u, 0u, 0u};
-    if (tid < 64) reinterpret_cast<uint32_t*>(sm[CB_NBUF - 1].vs)[tid] = 0u;
-  }
   __syncthreads();
-  if (!kLeaky) {
-    // Software pipeline: iteration it runs the softmax of tile it on scores computed one iteration
-    // earlier, with the next tile's score MFMAs and the previous tile's P.V MFMAs interleaved. Tile it
-    // lives in ring slot it % 4; tile it + 2 is loaded during iteration it straight into the slot of
-    // tile it - 2, which no wave reads after the barrier that ended iteration it - 1.
-    const int nfull = e_w / CB_BN;                   // full tiles of this wave
-    const int nt_w = nfull + (e_w % CB_BN ? 1 : 0);  // tiles with completed keys of this wave
-    v16f sa[2], sb[2];
-    if (nt_w > 0) {
-      if (nfull > 0)
-        scores<true>(sa, sm[0], qop, qsc, c, hf);
-      else
-        scores<false>(sa, sm[0], qop, qsc, c, hf);
-    }
-    // Deferred P codes and this lane's E8M0 byte: tile j's in (pb, spb) for even j, (pa, spa) for odd j
-    // (zero codes for tile -1).
-    v8i pa = {}, pb = {};
-    int spa = 127, spb = 127;
-    // Iteration it with its ring slots known at compile time (s = it % 4): the tile it + 2 load goes
-    // to slot (s + 2) % 4, and the LDS addresses of the iteration are constants off per-lane bases.
-    auto step = [&](auto kslot, int it, v16f(&sc)[2], v16f(&sn)[2], const v8i& pin, int sin, v8i& pout, int& sout) {
-      constexpr int s = decltype(kslot)::value;
-      const int kt0 = it * CB_BN;
-      if (it + 2 < ntiles) TILE_LOAD(sm[(s + 2) % CB_NBUF], psc, kt0 + 2 * CB_BN);
-      const TileSmem& cur = sm[s];
-      const TileSmem& nxt = sm[(s + 1) % CB_NBUF];
-      const TileSmem& prv = sm[(s + CB_NBUF - 1) % CB_NBUF];
-      if (it < nfull) {
-        if (it + 1 < nfull)
-          softmax_pv<true, 2, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
-                                        it == 0);
-        else if (it + 1 < nt_w)
-          softmax_pv<true, 1, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
-                                        it == 0);
-        else
-          softmax_pv<true, 0, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
-                                        it == 0);
-      } else if (it < nt_w) {
-        softmax_pv<false, 0, -1, true>(st, sc, cur, sn, nxt, prv, pin, sin, pout, sout, qop, qsc, scale_log2, c, hf,
-                                       it == 0);
-      } else if (it == nt_w && nt_w > 0) {
-        pv_deferred(st, prv, pin, sin, c, hf);  // the P.V of the wave's last tile
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      if (it + 2 < ntiles) store_scales(sm[(s + 2) % CB_NBUF], psc, tid);
-      __syncthreads();
-    };
-    // unrolled by four: the slots are constants, and the score and P buffers swap roles without copies
-    for (int it = 0; it < ntiles; it += 4) {
-      step(std::integral_constant<int, 0>{}, it, sa, sb, pa, spa, pb, spb);
-      if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1, sb, sa, pb, spb, pa, spa);
-      if (it + 2 < ntiles) step(std::integral_constant<int, 2>{}, it + 2, sa, sb, pa, spa, pb, spb);
-      if (it + 3 < ntiles) step(std::integral_constant<int, 3>{}, it + 3, sb, sa, pb, spb, pa, spa);
-    }
-    if (nt_w == ntiles && nt_w > 0) {
-      if ((ntiles - 1) & 1)
-        pv_deferred(st, sm[(ntiles - 1) % CB_NBUF], pa, spa, c, hf);
-      else
-        pv_deferred(st, sm[(ntiles - 1) % CB_NBUF], pb, spb, c, hf);
-    }
-    __syncthreads();  // every wave's deferred LDS reads are done before the epilogue reuses the LDS
-  }
-  // Ordinary causal variant: the plain loop (no next-tile scores), the own block masked per element.
-  for (int it = 0; kLeaky && it < ntiles; ++it) {
+  // One 64-key tile per iteration, double-buffered. The score MFMAs of tile it come first; then the
+  // loads of tile it + 1 into the other buffer (last read before the barrier that ended iteration
+  // it - 1); then the softmax and P.V. The first LDS read after those loads is the P.V operand read at
+  // the end of the softmax, so the wait for them (which the compiler places before any later LDS
+  // read) hides under the softmax.
+  for (int it = 0; it < ntiles; ++it) {
     const int kt0 = it * CB_BN;
-    // Prefetch the next tile straight into the other buffer (not read in this iteration).
-    if (it + 1 < ntiles) TILE_LOAD(sm[(it + 1) & 1], psc, kt0 + CB_BN);
     const TileSmem& cur = sm[it & 1];
-    v16f sacc[2], none[2];
-    v8i nop8 = {};
-    int nsc = 127;
-    if (kt0 + CB_BN <= e_w) {
+    // The keys of this tile the wave attends: all 64 (full) or the first 32-key block (half); in the
+    // ordinary causal variant also a completed block followed by the own block, masked per element
+    // (own2), or the own block alone (own1).
+    const bool full = kt0 + CB_BN <= e_w;
+    const bool half = !kLeaky && !full && kt0 < e_w;
+    const bool own2 = kLeaky && !full && kt0 < e_w;
+    const bool own1 = kLeaky && wave_valid && kt0 == e_w;
+    v16f sacc[2];
+    if (full || own2)
       scores<true>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<true>(st, sacc, cur, none, cur, cur, nop8, nsc, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
-    } else if (kt0 < e_w) {  // completed block, then the own block (masked)
-      scores<true>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<true, 0, 1>(st, sacc, cur, none, cur, cur, nop8, nsc, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
-    } else if (wave_valid && kt0 == e_w) {  // the own block opens this tile (masked)
+    else if (half || own1)
       scores<false>(sacc, cur, qop, qsc, c, hf);
-      softmax_pv<false, 0, 0>(st, sacc, cur, none, cur, cur, nop8, nsc, nop8, nsc, qop, qsc, scale_log2, c, hf, it == 0);
-    }
+    if (it + 1 < ntiles) TILE_LOAD(sm[(it + 1) & 1], psc, kt0 + CB_BN);
+    if (full)
+      softmax_pv<true>(st, sacc, cur, scale_log2, c, hf, it == 0);
+    else if (half)
+      softmax_pv<false>(st, sacc, cur, scale_log2, c, hf, it == 0);
+    else if (own2)
+      softmax_pv<true, 1>(st, sacc, cur, scale_log2, c, hf, it == 0);
+    else if (own1)
+      softmax_pv<false, 0>(st, sacc, cur, scale_log2, c, hf, it == 0);
     // The next tile's loads (LDS and scale word) are complete here on every path; then its scales
     // are stored and the barrier publishes the tile.
     __builtin_amdgcn_s_waitcnt(0x0F70);
