@@ -44,6 +44,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 
 namespace mxfa {
 
@@ -444,9 +446,12 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
   // it - 1); then the softmax and P.V. The first LDS read after those loads is the P.V operand read at
   // the end of the softmax, so the wait for them (which the compiler places before any later LDS
   // read) hides under the softmax.
-  for (int it = 0; it < ntiles; ++it) {
+  // Iteration it with its buffer known at compile time (s = it % 2), so that the LDS addresses of the
+  // iteration are immediate offsets from per-lane bases; the loop is unrolled by two.
+  auto step = [&](auto kslot, int it) {
+    constexpr int s = decltype(kslot)::value;
     const int kt0 = it * CB_BN;
-    const TileSmem& cur = sm[it & 1];
+    const TileSmem& cur = sm[s];
     // The keys of this tile the wave attends: all 64 (full) or the first 32-key block (half); in the
     // ordinary causal variant also a completed block followed by the own block, masked per element
     // (own2), or the own block alone (own1).
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
       scores<true>(sacc, cur, qop, qsc, c, hf);
     else if (half || own1)
       scores<false>(sacc, cur, qop, qsc, c, hf);
-    if (it + 1 < ntiles) TILE_LOAD(sm[(it + 1) & 1], psc, kt0 + CB_BN);
+    if (it + 1 < ntiles) TILE_LOAD(sm[s ^ 1], psc, kt0 + CB_BN);
     if (full)
       softmax_pv<true>(st, sacc, cur, scale_log2, c, hf, it == 0);
     else if (half)
@@ -471,8 +476,12 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
     // The next tile's loads (LDS and scale word) are complete here on every path; then its scales
     // are stored and the barrier publishes the tile.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (it + 1 < ntiles) store_scales(sm[(it + 1) & 1], psc, tid);
+    if (it + 1 < ntiles) store_scales(sm[s ^ 1], psc, tid);
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   float la = st.lsum, lb = st.lsum;
