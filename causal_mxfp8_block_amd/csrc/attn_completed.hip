@@ -57,7 +57,8 @@ constexpr int CB_BN = 64;     // keys per tile (two 32-key MX blocks)
 // column d in slot x ^ ((d >> 2) & 3).
 constexpr int CB_KROW = 128;  // LDS bytes per K row
 constexpr int CB_VROW = 64;   // LDS bytes per V column (keys contiguous)
-constexpr float CB_PMAX_LAZY = 256.0f;  // raise T once a block maximum of p exceeds 2^8
+constexpr float CB_LOG2_PMAX_LAZY = 8.0f;  // raise T once a block maximum of p exceeds 2^8
+constexpr float CB_LOG2_448 = 8.80735492205760410f;  // log2 of the largest E4M3 value
 constexpr int CB_RSRC_W3 = 0x00020000;  // buffer descriptor word 3 on gfx9: 32-bit data, raw offsets
 
 struct __align__(16) TileSmem {
@@ -222,10 +223,11 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
   float M0 = vmax(m0, m1), M1 = M0;
   swap32f(M0, M1);
   float negT = -st.T;
-  float pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
-  float pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
-  if (first || __any(vmax(pm0, pm1) > CB_PMAX_LAZY)) {
-    const float shift = ceilf(fmaf(kFull ? vmax(M0, M1) : M0, scale_log2, negT));
+  // log2 of each block's largest p = 2^(t - T) (fma is monotone, so the largest score gives it)
+  float x0 = fmaf(M0, scale_log2, negT);
+  float x1 = kFull ? fmaf(M1, scale_log2, negT) : -INFINITY;
+  if (first || __any(vmax(x0, x1) > CB_LOG2_PMAX_LAZY)) {
+    const float shift = ceilf(vmax(x0, x1));
     const float f = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -234,13 +236,15 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     st.lsum *= f;
     st.T += shift;
     negT = -st.T;
-    pm0 = __builtin_amdgcn_exp2f(fmaf(M0, scale_log2, negT));
-    pm1 = kFull ? __builtin_amdgcn_exp2f(fmaf(M1, scale_log2, negT)) : 0.f;
+    x0 = fmaf(M0, scale_log2, negT);
+    x1 = kFull ? fmaf(M1, scale_log2, negT) : -INFINITY;
   }
-  const int e0 = max((int)((f2u(pm0) + 0x1FFFFFu) >> 23), 9) - 8;
-  const int e1 = kFull ? max((int)((f2u(pm1) + 0x1FFFFFu) >> 23), 9) - 8 : 1;
-  const float t127 = 127.f - st.T;
-  const float nb0 = t127 - (float)e0, nb1 = t127 - (float)e1;
+  // E8M0 exponent of each block of P: the smallest k with max p <= 448 * 2^k, k = ceil(log2(max p) -
+  // log2 448), floored at -126; nb = -T - k folds it into the exponential, e = k + 127 is the byte.
+  const float k0 = vmax(ceilf(x0 - CB_LOG2_448), -126.f);
+  const float k1 = kFull ? vmax(ceilf(x1 - CB_LOG2_448), -126.f) : -126.f;
+  const float nb0 = negT - k0, nb1 = negT - k1;
+  const int e0 = (int)k0 + 127, e1 = (int)k1 + 127;
 
   v8i pop;
   float ls0 = 0.f, ls1 = 0.f;
