@@ -488,6 +488,10 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
     if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
+  // This lane's query row (used below only by valid waves, for which e_w = qw), derived here from
+  // values the loop keeps live anyway, so that no row offset from before the loop has to be kept.
+  int qr = e_w + c;
+  asm("" : "+v"(qr));
   float la = st.lsum, lb = st.lsum;
   swap32f(la, lb);
   const float lc_tot = la + lb;       // l of the completed partial (both lane halves)
@@ -497,7 +501,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
     // O = acc / l and lse of the ordinary causal row (every row has at least its own key)
     if (!wave_valid) return;
     const float inv = 1.0f / lc_tot;
-    const int64_t off = b * P.osb + (int64_t)(qw + c) * P.oss + hq * P.osh + 4 * hf;
+    const int64_t off = b * P.osb + (int64_t)qr * P.oss + hq * P.osh + 4 * hf;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -515,11 +519,11 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(P.out) + o) = make_float4(r[0], r[1], r[2], r[3]);
         }
       }
-    if (hf == 0 && P.lse_out) P.lse_out[bhq * S + qw + c] = (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
+    if (hf == 0 && P.lse_out) P.lse_out[bhq * S + qr] = (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
     return;
   } else if (!kFused) {
     if (!wave_valid) return;
-    float* orow = P.o_c + (bhq * S + qw + c) * 128;
+    float* orow = P.o_c + (bhq * S + qr) * 128;
     const float inv = empty ? 0.f : 1.0f / lc_tot;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
                                        st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv);
         *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * hf) = val;
       }
-    if (hf == 0) P.lse_c[bhq * S + qw + c] = empty ? -INFINITY : (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
+    if (hf == 0) P.lse_c[bhq * S + qr] = empty ? -INFINITY : (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
     return;
   } else {
     // ---- own block: keys qw .. qw+31, query qw + c sees keys up to itself ----------------------
@@ -605,7 +609,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
     const float wo = __builtin_amdgcn_exp2f(l2o - M);
     const float inv = 1.0f / (wc + wo);
     const float fc = empty ? 0.f : wc * inv / lc_tot, fo = wo * inv / lo;
-    const int q = qw + c;
+    const int q = qr;
     const int64_t off = b * P.osb + (int64_t)q * P.oss + hq * P.osh + 4 * hf;
     // ---- own O^T = V^T P^T in fp32 with v_mfma_f32_32x32x2_f32 ---------------------------------
     // Step u contracts the two keys 8(u/4) + (u%4) (k = 0) and 8(u/4) + 4 + (u%4) (k = 1): lane
