@@ -46,10 +46,12 @@ def _partials_case(inp, rows=None):
     return (goc, glc, goo, glo), (roc, rlc, roo, rlo, ral)
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 1, 128), (2, 4, 2, 416), (1, 8, 2, 288), (1, 2, 1, 32), (1, 3, 1, 96)])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 128), (2, 4, 2, 416), (1, 8, 2, 288), (1, 2, 1, 32), (1, 3, 1, 96),
+                                   (1, 4, 2, 352)])
 def test_partials_small(shape):
     """Both partials on shapes spanning several 128-query tiles, ragged tails (S % 128 != 0), GQA and
-    batch, compared with the oracle on every row."""
+    batch, and odd numbers of 64-key tiles per workgroup (S = 352: five for the third query tile),
+    compared with the oracle on every row."""
     B, Hq, Hkv, S = shape
     inp = make_inputs(custom(B, Hq, Hkv, S, values="outliers", seed=sum(shape)))
     say(f"partials {shape}")

@@ -34,7 +34,8 @@ def _oracle_leaky(inp, rows=None):
     return oracle.attn_leaky(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale, rows, allowance=True)
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 1, 128), (2, 4, 2, 416), (1, 8, 2, 288), (1, 2, 1, 32), (1, 3, 1, 96)])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 128), (2, 4, 2, 416), (1, 8, 2, 288), (1, 2, 1, 32), (1, 3, 1, 96),
+                                   (1, 4, 2, 352)])
 def test_leaky_matches_oracle_small(shape):
     """Every row of shapes spanning several query tiles, ragged tails, GQA and batch > 1 (both own-block
     positions in a 64-key tile occur)."""
