@@ -19,8 +19,8 @@
 //    raised only when a block maximum of p would exceed 2^8 (lazy rescale); the E8M0 quantisation of P
 //    commutes with powers of two, so the P codes do not depend on T.
 //  * The E8M0 exponent of each (query, 32-key block) of P comes from the block maximum taken on the
-//    raw scores: fma and v_exp_f32 are both monotone (the latter checked exhaustively on [-160, 10]),
-//    so 2^(max t - T) is exactly the largest p of the block. The block's exponent k is then folded
+//    raw scores: the fma that forms t is monotone, so x = max t - T is log2 of the block's largest p,
+//    and k = ceil(x - log2 448) is the smallest k with max p <= 448 * 2^k. The exponent is then folded
 //    into the exponential, p / 2^k = 2^(t - T - k), so the plain v_cvt_pk_fp8_f32 gives the E4M3
 //    codes; the normaliser sums p / 2^k per block and rescales the two block sums by 2^k. P.V is
 //    the block-scaled FP8 MFMA again, on the columnwise V codes (keys contiguous per column).
@@ -45,7 +45,6 @@
 #include "launch.h"
 
 #include <type_traits>
-
 
 namespace mxfa {
 
