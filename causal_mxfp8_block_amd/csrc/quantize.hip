@@ -49,98 +49,85 @@ __global__ __launch_bounds__(256) void quantize_rowwise_kernel(const uint16_t* _
   if ((part & 3) == 0) scales[orow * 4 + (part >> 2)] = (uint8_t)(k + 127);
 }
 
-// One wave per (b, h, 32-token block): the bf16 block is staged in LDS once and read twice, by rows
-// (token-normalised copy) and by columns (the columnwise block of each head-dim column). Small
-// single-wave workgroups keep many blocks in different phases at once, so HBM reads and writes
-// overlap across them.
-constexpr int VQ_TOK = 32;
+// One workgroup per (b, h, group of up to 128 tokens): the bf16 tile is staged in LDS once and read
+// twice, by rows (token-normalised copy) and by columns (columnwise blocks).
+constexpr int VQ_TOK = 128;
 constexpr int VQ_ROW = 128 + 8;  // bf16 elements per LDS row (padding spreads banks)
 
-__global__ __launch_bounds__(64) void quantize_v_kernel(const uint16_t* __restrict__ v, int S, int H, int64_t sb,
-                                                        int64_t ss, int64_t sh, uint8_t* __restrict__ col_codes,
-                                                        uint8_t* __restrict__ col_scales,
-                                                        uint8_t* __restrict__ tn_codes,
-                                                        uint8_t* __restrict__ tn_amps) {
+__global__ __launch_bounds__(256) void quantize_v_kernel(const uint16_t* __restrict__ v, int S, int H, int64_t sb,
+                                                         int64_t ss, int64_t sh, uint8_t* __restrict__ col_codes,
+                                                         uint8_t* __restrict__ col_scales,
+                                                         uint8_t* __restrict__ tn_codes,
+                                                         uint8_t* __restrict__ tn_amps) {
   __shared__ __align__(16) uint16_t tile[VQ_TOK * VQ_ROW];
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int s0 = blockIdx.x * VQ_TOK, h = blockIdx.y, b = blockIdx.z;
+  const int ntok = min(VQ_TOK, S - s0);  // a multiple of 32
   const int64_t bh = (int64_t)b * H + h;
-  // 32 rows x 16 chunks of 16 bytes: lane takes chunks lane + 64 i, four whole rows per instruction
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = lane + 64 * i, r = c >> 4, q = c & 15;
+  for (int c = tid; c < ntok * 16; c += 256) {
+    const int r = c >> 4, q = c & 15;
     const uint4 val = *reinterpret_cast<const uint4*>(v + b * sb + (int64_t)(s0 + r) * ss + h * sh + q * 8);
     *reinterpret_cast<uint4*>(tile + r * VQ_ROW + q * 8) = val;
   }
   __syncthreads();
 
-  // Token-normalised copy: two lanes per token, 64 elements each.
+  // Token-normalised copy: two threads per token, 64 elements each.
   if (tn_codes) {
-    const int r = lane >> 1, half = lane & 1;
-    const uint16_t* src = tile + r * VQ_ROW + half * 64;
-    float x[64];
+    const int r = tid >> 1, half = tid & 1;
+    if (r < ntok) {
+      const uint16_t* src = tile + r * VQ_ROW + half * 64;
+      float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * i);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(src[i])));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      const int k = e8m0_exponent(amax);
+      const float m = pow2_neg(k);
+      uint8_t* dst = tn_codes + (bh * S + s0 + r) * 128 + half * 64;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[8 * i + 2 * j] = bf16_to_f32(ww[j] & 0xffffu);
-        x[8 * i + 2 * j + 1] = bf16_to_f32(ww[j] >> 16);
+      for (int i = 0; i < 64; i += 16) {
+        uint4 o;
+        o.x = pack4_e4m3(bf16_to_f32(src[i + 0]) * m, bf16_to_f32(src[i + 1]) * m, bf16_to_f32(src[i + 2]) * m,
+                         bf16_to_f32(src[i + 3]) * m);
+        o.y = pack4_e4m3(bf16_to_f32(src[i + 4]) * m, bf16_to_f32(src[i + 5]) * m, bf16_to_f32(src[i + 6]) * m,
+                         bf16_to_f32(src[i + 7]) * m);
+        o.z = pack4_e4m3(bf16_to_f32(src[i + 8]) * m, bf16_to_f32(src[i + 9]) * m, bf16_to_f32(src[i + 10]) * m,
+                         bf16_to_f32(src[i + 11]) * m);
+        o.w = pack4_e4m3(bf16_to_f32(src[i + 12]) * m, bf16_to_f32(src[i + 13]) * m, bf16_to_f32(src[i + 14]) * m,
+                         bf16_to_f32(src[i + 15]) * m);
+        *reinterpret_cast<uint4*>(dst + i) = o;
       }
+      if (half == 0) tn_amps[bh * S + s0 + r] = (uint8_t)(k + 127);
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    const int k = e8m0_exponent(amax);
-    const float m = pow2_neg(k);
-    uint8_t* dst = tn_codes + (bh * S + s0 + r) * 128 + half * 64;
-#pragma unroll
-    for (int i = 0; i < 64; i += 16) {
-      uint4 o;
-      o.x = pack4_e4m3(x[i + 0] * m, x[i + 1] * m, x[i + 2] * m, x[i + 3] * m);
-      o.y = pack4_e4m3(x[i + 4] * m, x[i + 5] * m, x[i + 6] * m, x[i + 7] * m);
-      o.z = pack4_e4m3(x[i + 8] * m, x[i + 9] * m, x[i + 10] * m, x[i + 11] * m);
-      o.w = pack4_e4m3(x[i + 12] * m, x[i + 13] * m, x[i + 14] * m, x[i + 15] * m);
-      *reinterpret_cast<uint4*>(dst + i) = o;
-    }
-    if (half == 0) tn_amps[bh * S + s0 + r] = (uint8_t)(k + 127);
   }
 
-  // Columnwise block of the 32 tokens: lane takes columns d = 2 lane and 2 lane + 1, reading one dword
-  // (both columns) per row, so each row read is 256 contiguous bytes across the wave.
+  // Columnwise blocks: item = (d, u); four adjacent threads hold the four token blocks of one
+  // column, so together they write 128 contiguous code bytes.
   if (col_codes) {
-    float x0[32], x1[32];
-    float a0 = 0.f, a1 = 0.f;
+    const int nblk = ntok >> 5;
+    for (int item = tid; item < 128 * 4; item += 256) {
+      const int u = item & 3, d = item >> 2;
+      if (u >= nblk) continue;
+      float x[32];
+      float amax = 0.f;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(tile + r * VQ_ROW + 2 * lane);
-      x0[r] = bf16_to_f32(w & 0xffffu);
-      x1[r] = bf16_to_f32(w >> 16);
-      a0 = fmaxf(a0, fabsf(x0[r]));
-      a1 = fmaxf(a1, fabsf(x1[r]));
-    }
-    const int k0 = e8m0_exponent(a0), k1 = e8m0_exponent(a1);
-    const float m0 = pow2_neg(k0), m1 = pow2_neg(k1);
-    uint8_t* dst0 = col_codes + (bh * 128 + 2 * lane) * S + s0;
-    uint8_t* dst1 = dst0 + S;
+      for (int r = 0; r < 32; ++r) {
+        x[r] = bf16_to_f32(tile[(32 * u + r) * VQ_ROW + d]);
+        amax = fmaxf(amax, fabsf(x[r]));
+      }
+      const int k = e8m0_exponent(amax);
+      const float m = pow2_neg(k);
+      uint8_t* dst = col_codes + (bh * 128 + d) * S + s0 + 32 * u;
 #pragma unroll
-    for (int r = 0; r < 32; r += 16) {
-      uint4 o0, o1;
-      o0.x = pack4_e4m3(x0[r + 0] * m0, x0[r + 1] * m0, x0[r + 2] * m0, x0[r + 3] * m0);
-      o0.y = pack4_e4m3(x0[r + 4] * m0, x0[r + 5] * m0, x0[r + 6] * m0, x0[r + 7] * m0);
-      o0.z = pack4_e4m3(x0[r + 8] * m0, x0[r + 9] * m0, x0[r + 10] * m0, x0[r + 11] * m0);
-      o0.w = pack4_e4m3(x0[r + 12] * m0, x0[r + 13] * m0, x0[r + 14] * m0, x0[r + 15] * m0);
-      o1.x = pack4_e4m3(x1[r + 0] * m1, x1[r + 1] * m1, x1[r + 2] * m1, x1[r + 3] * m1);
-      o1.y = pack4_e4m3(x1[r + 4] * m1, x1[r + 5] * m1, x1[r + 6] * m1, x1[r + 7] * m1);
-      o1.z = pack4_e4m3(x1[r + 8] * m1, x1[r + 9] * m1, x1[r + 10] * m1, x1[r + 11] * m1);
-      o1.w = pack4_e4m3(x1[r + 12] * m1, x1[r + 13] * m1, x1[r + 14] * m1, x1[r + 15] * m1);
-      *reinterpret_cast<uint4*>(dst0 + r) = o0;
-      *reinterpret_cast<uint4*>(dst1 + r) = o1;
+      for (int r = 0; r < 32; r += 16) {
+        uint4 o;
+        o.x = pack4_e4m3(x[r + 0] * m, x[r + 1] * m, x[r + 2] * m, x[r + 3] * m);
+        o.y = pack4_e4m3(x[r + 4] * m, x[r + 5] * m, x[r + 6] * m, x[r + 7] * m);
+        o.z = pack4_e4m3(x[r + 8] * m, x[r + 9] * m, x[r + 10] * m, x[r + 11] * m);
+        o.w = pack4_e4m3(x[r + 12] * m, x[r + 13] * m, x[r + 14] * m, x[r + 15] * m);
+        *reinterpret_cast<uint4*>(dst + r) = o;
+      }
+      col_scales[(bh * (S / 32) + s0 / 32 + u) * 128 + d] = (uint8_t)(k + 127);
     }
-    *reinterpret_cast<uint16_t*>(col_scales + (bh * (S / 32) + s0 / 32) * 128 + 2 * lane) =
-        (uint16_t)((k0 + 127) | ((k1 + 127) << 8));
   }
 }
 
@@ -156,8 +143,8 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int B, int S, int H, int64
 hipError_t launch_quantize_v(const uint16_t* v, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
                              uint8_t* col_codes, uint8_t* col_scales, uint8_t* tn_codes, uint8_t* tn_amps,
                              hipStream_t stream) {
-  dim3 grid((unsigned)(S / VQ_TOK), (unsigned)H, (unsigned)B);  // S % 32 == 0 (checked by the caller)
-  quantize_v_kernel<<<grid, dim3(64), 0, stream>>>(v, S, H, sb, ss, sh, col_codes, col_scales, tn_codes, tn_amps);
+  dim3 grid((unsigned)((S + VQ_TOK - 1) / VQ_TOK), (unsigned)H, (unsigned)B);
+  quantize_v_kernel<<<grid, dim3(256), 0, stream>>>(v, S, H, sb, ss, sh, col_codes, col_scales, tn_codes, tn_amps);
   return hipGetLastError();
 }
 
