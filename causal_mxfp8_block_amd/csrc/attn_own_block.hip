@@ -20,9 +20,12 @@ __global__ __launch_bounds__(256) void own_block_kernel(const uint8_t* __restric
                                                         const uint8_t* __restrict__ vta, int S, int Hq, int Hkv,
                                                         float scale, float* __restrict__ o,
                                                         float* __restrict__ lse) {
-  __shared__ float Qm[32][129];
-  __shared__ float Km[32][129];
-  __shared__ float Vm[32][128];
+  // Q and K rows unpadded (52 KB in all, three workgroups per CU); float4 chunk x of Q row r sits in
+  // slot x ^ (r & 7), of K row r in slot x ^ ((r >> 2) & 7): the eight Q rows (i) and the eight K rows
+  // (4k + jj) that one wave reads at a time fall in different banks
+  __shared__ __align__(16) float Qm[32][128];
+  __shared__ __align__(16) float Km[32][128];
+  __shared__ __align__(16) float Vm[32][128];
   __shared__ float P[32][33];
   const int tid = threadIdx.x;
   const int cb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -38,38 +41,64 @@ __global__ __launch_bounds__(256) void own_block_kernel(const uint8_t* __restric
     const float sq = e8m0_to_f32(qs[(qrow0 + r) * 4 + (d4 >> 5)]);
     const float sk = e8m0_to_f32(ks[(krow0 + r) * 4 + (d4 >> 5)]);
     const float sv = e8m0_to_f32(vta[krow0 + r]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Qm[r][d4 + i] = e4m3_to_f32((cq >> (8 * i)) & 0xffu) * sq;
-      Km[r][d4 + i] = e4m3_to_f32((ck >> (8 * i)) & 0xffu) * sk;
-      Vm[r][d4 + i] = e4m3_to_f32((cv >> (8 * i)) & 0xffu) * sv;
-    }
+    // v_cvt_pk_f32_fp8 decodes two OCP E4M3 codes exactly (every code checked on gfx950)
+    const auto q01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cq, false), q23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cq, true);
+    const auto k01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ck, false), k23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ck, true);
+    const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cv, false), v23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cv, true);
+    *reinterpret_cast<float4*>(&Qm[r][4 * ((d4 >> 2) ^ (r & 7))]) =
+        make_float4(q01[0] * sq, q01[1] * sq, q23[0] * sq, q23[1] * sq);
+    *reinterpret_cast<float4*>(&Km[r][4 * ((d4 >> 2) ^ ((r >> 2) & 7))]) =
+        make_float4(k01[0] * sk, k01[1] * sk, k23[0] * sk, k23[1] * sk);
+    *reinterpret_cast<float4*>(&Vm[r][d4]) = make_float4(v01[0] * sv, v01[1] * sv, v23[0] * sv, v23[1] * sv);
   }
   __syncthreads();
-  {  // scores: thread -> (query i, four keys)
+  {  // scores: thread -> (query i, four keys), each dot product accumulated in order of d
     const int i = tid >> 3, jg = (tid & 7) * 4;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < 128; d += 4) {
+      const float4 qv = *reinterpret_cast<const float4*>(&Qm[i][4 * ((d >> 2) ^ (i & 7))]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = jg + jj;
+        const float4 kv = *reinterpret_cast<const float4*>(&Km[j][4 * ((d >> 2) ^ ((j >> 2) & 7))]);
+        acc[jj] = fmaf(qv.x, kv.x, acc[jj]);
+        acc[jj] = fmaf(qv.y, kv.y, acc[jj]);
+        acc[jj] = fmaf(qv.z, kv.z, acc[jj]);
+        acc[jj] = fmaf(qv.w, kv.w, acc[jj]);
+      }
+    }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = jg + jj;
-      float acc = 0.f;
-      for (int d = 0; d < 128; ++d) acc = fmaf(Qm[i][d], Km[j][d], acc);
-      P[i][j] = (j <= i) ? acc * scale : -INFINITY;
+      P[i][j] = (j <= i) ? acc[jj] * scale : -INFINITY;
     }
   }
   __syncthreads();
-  if (tid < 32) {  // softmax of row i over keys 0..i
-    const int i = tid;
+  {  // softmax of row i over keys 0..i: the row's eight consecutive lanes take four keys each
+    const int i = tid >> 3, jg = (tid & 7) * 4;
+    float v[4];
     float m = -INFINITY;
-    for (int j = 0; j <= i; ++j) m = fmaxf(m, P[i][j]);
-    float l = 0.f;
-    for (int j = 0; j < 32; ++j) {
-      const float p = (j <= i) ? expf(P[i][j] - m) : 0.f;
-      P[i][j] = p;
-      l += p;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      v[jj] = P[i][jg + jj];  // -inf for keys after the query
+      m = fmaxf(m, v[jj]);
     }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    float l = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      v[jj] = (jg + jj <= i) ? expf(v[jj] - m) : 0.f;
+      l += v[jj];
+    }
+    l += __shfl_xor(l, 1);
+    l += __shfl_xor(l, 2);
+    l += __shfl_xor(l, 4);
     const float inv = 1.0f / l;
-    for (int j = 0; j <= i; ++j) P[i][j] *= inv;
-    lse[qrow0 + i] = m + logf(l);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) P[i][jg + jj] = v[jj] * inv;
+    if ((tid & 7) == 0) lse[qrow0 + i] = m + logf(l);
   }
   __syncthreads();
   {  // output: thread -> (query i, 16 columns)
