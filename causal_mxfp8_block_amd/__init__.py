@@ -257,7 +257,9 @@ def attn_fwd_workspace_bytes(B: int, S: int, Hq: int, Hkv: int, D: int = 128) ->
 
 def attn_fwd(q, k, v, softmax_scale: float | None = None, layout: str = "bshd", out_dtype=torch.bfloat16,
              workspace=None, out=None, lse=None):
-    """The whole leak-free forward in one call (quantise Q, K, V; then the fused attention).
+    """The whole leak-free forward in one call: K quantised rowwise and V columnwise plus
+    token-normalised into the workspace, then the fused attention kernel, which quantises Q itself
+    (rowwise, the same codes and scales as mxfp8_quantize) and writes O and the LSE.
 
     q [B,S,Hq,D], k and v [B,S,Hkv,D] bf16 in ``layout``; returns (out in q's layout, lse [B,Hq,S])."""
     B, S, Hq, D, qsb, qss, qsh = view_of(q, layout)

@@ -54,9 +54,14 @@ int check_device() {
   return MXFA_OK;
 }
 
+// Largest sequence length: the attention kernels address one (b, head) slice of codes, S * 128 bytes,
+// through a buffer resource whose record count is 32 bits, with 32-bit offsets inside it.
+constexpr int kMaxS = 1 << 24;
+
 int check_attn_shape(int B, int S, int Hq, int Hkv, int D) {
   if (D != 128) return fail(MXFA_ERR_UNSUPPORTED, "D = %d: only D = 128 is supported", D);
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return fail(MXFA_ERR_SHAPE, "B, S, Hq, Hkv must be >= 1");
+  if (S > kMaxS) return fail(MXFA_ERR_SHAPE, "S = %d exceeds the largest supported length 2^24", S);
   if (S % 32 != 0) return fail(MXFA_ERR_SHAPE, "S = %d is not a multiple of 32", S);
   if (Hq % Hkv != 0) return fail(MXFA_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
   if ((int64_t)B * Hq > 65535 * 64 || Hq > 65535 || B > 65535 ||
@@ -171,6 +176,7 @@ MXFA_EXPORT int mxfa_mxfp8_quantize(const void* x, int B, int S, int H, int D, i
   g_last_error.clear();
   if (D != 128) return fail(MXFA_ERR_UNSUPPORTED, "D = %d: only D = 128 is supported", D);
   if (B < 1 || S < 1 || H < 1) return fail(MXFA_ERR_SHAPE, "B, S, H must be >= 1");
+  if (S > kMaxS) return fail(MXFA_ERR_SHAPE, "S = %d exceeds the largest supported length 2^24", S);
   if (B > 65535 || H > 65535) return fail(MXFA_ERR_SHAPE, "B = %d, H = %d exceed the launch grid", B, H);
   TRY(check_view("x", x, B, S, H, sb, ss, sh, 8));
   if (mode == MXFA_QUANT_ROWWISE) {
@@ -240,6 +246,7 @@ MXFA_EXPORT int mxfa_lse_merge(const float* o_c, const float* lse_c, const float
   g_last_error.clear();
   if (D != 128) return fail(MXFA_ERR_UNSUPPORTED, "D = %d: only D = 128 is supported", D);
   if (B < 1 || S < 1 || H < 1) return fail(MXFA_ERR_SHAPE, "B, S, H must be >= 1");
+  if (S > kMaxS) return fail(MXFA_ERR_SHAPE, "S = %d exceeds the largest supported length 2^24", S);
   if (out_dtype != MXFA_OUT_BF16 && out_dtype != MXFA_OUT_F32)
     return fail(MXFA_ERR_UNSUPPORTED, "unknown output dtype %d", out_dtype);
   const char* n[] = {"o_c", "lse_c", "o_o", "lse_o"};
@@ -335,7 +342,7 @@ MXFA_EXPORT int mxfa_attn_fwd_leaky(const uint8_t* qc, const uint8_t* qs, const 
 }
 
 MXFA_EXPORT size_t mxfa_attn_fwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D) {
-  if (D != 128 || B < 1 || S < 1 || Hq < 1 || Hkv < 1) return 0;
+  if (D != 128 || B < 1 || S < 1 || S > kMaxS || Hq < 1 || Hkv < 1) return 0;
   return carve(nullptr, B, S, Hq, Hkv).bytes;
 }
 
@@ -371,7 +378,7 @@ MXFA_EXPORT int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t q
 }
 
 MXFA_EXPORT size_t mxfa_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D) {
-  if (D != 128 || B < 1 || S < 1 || Hq < 1 || Hkv < 1) return 0;
+  if (D != 128 || B < 1 || S < 1 || S > kMaxS || Hq < 1 || Hkv < 1) return 0;
   return carve_bwd(nullptr, B, S, Hq, Hkv).bytes;
 }
 

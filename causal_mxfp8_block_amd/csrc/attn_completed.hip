@@ -16,14 +16,16 @@
 //    B operand of O^T = V^T . P^T. The E4M3 codes of P therefore go into that MFMA where they were
 //    computed, with no cross-lane traffic.
 //  * Online softmax in the log2 domain with an integer running exponent T: p = 2^(t - T). T is
-//    raised only when a block maximum of p would exceed 2^8 (lazy rescale); the E8M0 quantisation of P
-//    commutes with powers of two, so the P codes do not depend on T.
+//    raised only when a block maximum of p would exceed 224 (lazy rescale); the E8M0 quantisation of
+//    P commutes with powers of two, so the P codes do not depend on T.
 //  * The E8M0 exponent of each (query, 32-key block) of P comes from the block maximum taken on the
-//    raw scores: the fma that forms t is monotone, so x = max t - T is log2 of the block's largest p,
-//    and k = ceil(x - log2 448) is the smallest k with max p <= 448 * 2^k. The exponent is then folded
-//    into the exponential, p / 2^k = 2^(t - T - k), so the plain v_cvt_pk_fp8_f32 gives the E4M3
-//    codes; the normaliser sums p / 2^k per block and rescales the two block sums by 2^k. P.V is
-//    the block-scaled FP8 MFMA again, on the columnwise V codes (keys contiguous per column).
+//    raw scores: the fma that forms t is monotone, so k = ceil(scale * max s - T - log2 448), one fma
+//    with -(T + log2 448) kept per lane, is the smallest k with max p <= 448 * 2^k. Lane half hf
+//    computes it for block hf, whose byte it supplies as the P.V scale operand, and one exchange
+//    gives every lane both. The exponent is then folded into the exponential, p / 2^k =
+//    2^(t - T - k), so the plain v_cvt_pk_fp8_f32 gives the E4M3 codes; the normaliser sums p / 2^k
+//    per block and rescales the two block sums by 2^k. P.V is the block-scaled FP8 MFMA again, on
+//    the columnwise V codes (keys contiguous per column).
 //  * O^T leaves one query per lane too, so the rescale and the final 1/l are per-lane scalars.
 //  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the LDS flag), once per
 //    workgroup, shared by the 4 waves: double-buffered, one barrier per tile. No register holds a
@@ -56,7 +58,6 @@ constexpr int CB_BN = 64;     // keys per tile (two 32-key MX blocks)
 // column d in slot x ^ ((d >> 2) & 3).
 constexpr int CB_KROW = 128;  // LDS bytes per K row
 constexpr int CB_VROW = 64;   // LDS bytes per V column (keys contiguous)
-constexpr float CB_LOG2_PMAX_LAZY = 8.0f;  // raise T once a block maximum of p exceeds 2^8
 constexpr float CB_LOG2_448 = 8.80735492205760410f;  // log2 of the largest E4M3 value
 constexpr int CB_RSRC_W3 = 0x00020000;  // buffer descriptor word 3 on gfx9: 32-bit data, raw offsets
 
@@ -161,7 +162,8 @@ __device__ __forceinline__ void store_scales(TileSmem& t, uint32_t sc, int tid) 
 // Per-wave running state of the online softmax.
 struct RowState {
   v16f o[4];   // O^T accumulator: lane (c, hf), element i of tile dt -> column 32dt + 8(i/4) + 4hf + i%4
-  float T;     // integer-valued running exponent (set on the wave's first tile)
+  float nT;    // -T: the integer-valued running exponent T, negated (set on the wave's first tile)
+  float nTL;   // -(T + log2 448)
   float lsum;  // this lane's share of sum p
 };
 
@@ -218,32 +220,38 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     m0 = vmax(m0, sacc[0][i]);
     if (kFull) m1 = vmax(m1, sacc[1][i]);
   }
+  // After the exchange lane half hf holds both halves of block hf's maximum (its own block: the one
+  // whose E8M0 byte it supplies as the P.V scale operand).
   swap32f(m0, m1);
-  float M0 = vmax(m0, m1), M1 = M0;
-  swap32f(M0, M1);
-  float negT = -st.T;
-  // log2 of each block's largest p = 2^(t - T) (fma is monotone, so the largest score gives it)
-  float x0 = fmaf(M0, scale_log2, negT);
-  float x1 = kFull ? fmaf(M1, scale_log2, negT) : -INFINITY;
-  if (first || __any(vmax(x0, x1) > CB_LOG2_PMAX_LAZY)) {
-    const float shift = ceilf(vmax(x0, x1));
+  const float Mown = vmax(m0, m1);
+  // E8M0 exponent of the own block of P: the smallest k with max p <= 448 * 2^k, with p = 2^(t - T)
+  // and the fma that forms t monotone, k = ceil(scale_log2 * max s - T - log2 448), clamped at
+  // -127 as the scale rule clamps it (byte 0). An empty block (-inf) gets -127.
+  float kown = vmax(ceilf(fmaf(Mown, scale_log2, st.nTL)), -127.f);
+  // Raise T when a block maximum of p would exceed 224 (k >= 0): lazy rescale by an exact power of
+  // two. After the first tile T only rises: a query whose maximum lies below its T keeps it, so its
+  // accumulator and sum are never scaled up (a large upward scale could overflow).
+  if (first || __any(kown >= 0.f)) {
+    float x0 = fmaf(Mown, scale_log2, st.nT), x1 = x0;  // log2 of each block's largest p
+    swap32f(x0, x1);
+    const float up = ceilf(vmax(x0, x1));
+    const float shift = first ? up : vmax(up, 0.f);
     const float f = first ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.o[dt][i] *= f;
     st.lsum *= f;
-    st.T += shift;
-    negT = -st.T;
-    x0 = fmaf(M0, scale_log2, negT);
-    x1 = kFull ? fmaf(M1, scale_log2, negT) : -INFINITY;
+    st.nT -= shift;
+    st.nTL -= shift;
+    kown = vmax(ceilf(fmaf(Mown, scale_log2, st.nTL)), -127.f);
   }
-  // E8M0 exponent of each block of P: the smallest k with max p <= 448 * 2^k, k = ceil(log2(max p) -
-  // log2 448), floored at -126; nb = -T - k folds it into the exponential, e = k + 127 is the byte.
-  const float k0 = vmax(ceilf(x0 - CB_LOG2_448), -126.f);
-  const float k1 = kFull ? vmax(ceilf(x1 - CB_LOG2_448), -126.f) : -126.f;
-  const float nb0 = negT - k0, nb1 = negT - k1;
-  const int e0 = (int)k0 + 127, e1 = (int)k1 + 127;
+  // The own block's byte is the P.V B-operand scale of this lane half; both exponents in every lane
+  // (k0, k1) for the elements: nb = -T - k folds the exponent into the exponential.
+  const int psc = (int)kown + 127;
+  float k0 = kown, k1 = kown;
+  swap32f(k0, k1);
+  const float nb0 = st.nT - k0, nb1 = st.nT - k1;
 
   v8i pop;
   float ls0 = 0.f, ls1 = 0.f;
@@ -267,8 +275,7 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
       pop[4 + g] = 0;
     }
   }
-  st.lsum += kFull ? ldexpf(ls0, e0 - 127) + ldexpf(ls1, e1 - 127) : ldexpf(ls0, e0 - 127);
-  const int psc = hf ? e1 : e0;
+  st.lsum += kFull ? ldexpf(ls0, (int)k0) + ldexpf(ls1, (int)k1) : ldexpf(ls0, (int)k0);
   // This tile's V^T operand of d-tile dt: lane (c, hf) supplies column 32dt + c, keys 16hf + [0,16) and
   // 32 + 16hf + [0,16); its scales are byte dt of the word of column c.
   const uint32_t vsw = *reinterpret_cast<const uint32_t*>(t.vs + hf * 128 + c * 4);
@@ -278,10 +285,15 @@ __device__ __forceinline__ void softmax_pv(RowState& st, v16f (&sacc)[2], const 
     return make_v8i(*reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, hf)),
                     *reinterpret_cast<const uint4*>(vr + 16 * v_slot(d, 2 + hf)));
   };
-  st.o[0] = mfma_mx<0, 0>(vop(0), pop, st.o[0], (int)vsw, psc);
-  st.o[1] = mfma_mx<1, 0>(vop(1), pop, st.o[1], (int)vsw, psc);
-  st.o[2] = mfma_mx<2, 0>(vop(2), pop, st.o[2], (int)vsw, psc);
-  st.o[3] = mfma_mx<3, 0>(vop(3), pop, st.o[3], (int)vsw, psc);
+  // All four V operands are read before the first P.V MFMA (the score registers are free by now), so
+  // the LDS latency is paid once rather than before each MFMA.
+  const v8i v0 = vop(0), v1 = vop(1), v2 = vop(2), v3 = vop(3);
+  __builtin_amdgcn_sched_group_barrier(0x0100, 9, 0);  // the 8 operand reads and the scale word
+  __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);  // then the 4 MFMAs
+  st.o[0] = mfma_mx<0, 0>(v0, pop, st.o[0], (int)vsw, psc);
+  st.o[1] = mfma_mx<1, 0>(v1, pop, st.o[1], (int)vsw, psc);
+  st.o[2] = mfma_mx<2, 0>(v2, pop, st.o[2], (int)vsw, psc);
+  st.o[3] = mfma_mx<3, 0>(v3, pop, st.o[3], (int)vsw, psc);
 }
 
 struct AttnParams {
@@ -345,14 +357,18 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
   // (the ordinary causal variant also reads the last wave's own block)
   const int ntiles = (e_wg + (kLeaky ? 32 : 0) + CB_BN - 1) / CB_BN;
   const int64_t bhq = (int64_t)b * P.Hq + hq, bhk = (int64_t)b * P.Hkv + hk;
-  // Buffer resources over this kv head's K codes [S,128], V codes [128,S] and K or V scales.
+  // Buffer resources over this kv head's K codes [S,128], V codes [128,S] and K or V scales. The
+  // record count is an unsigned 32-bit field: S <= 2^24 (checked on the host) keeps S * 128 <= 2^31
+  // and every per-lane and per-tile offset below it within a signed 32-bit int.
+  const int nrec_codes = (int)((uint32_t)S * 128u), nrec_scales = (int)((uint32_t)S * 4u);
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kc + bhk * S * 128), 0, S * 128, CB_RSRC_W3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kc + bhk * S * 128), 0, nrec_codes, CB_RSRC_W3);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vc + bhk * S * 128), 0, S * 128, CB_RSRC_W3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vc + bhk * S * 128), 0, nrec_codes, CB_RSRC_W3);
   const __amdgpu_buffer_rsrc_t rs =
-      wave_u == 0 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ks + bhk * S * 4), 0, S * 4, CB_RSRC_W3)
-                : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vcs + bhk * S * 4), 0, S * 4, CB_RSRC_W3);
+      wave_u == 0
+          ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(ks + bhk * S * 4), 0, nrec_scales, CB_RSRC_W3)
+          : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vcs + bhk * S * 4), 0, nrec_scales, CB_RSRC_W3);
   // Per-lane source offsets of the tile loads (the tile's own offset is a scalar): LDS chunk c of K is
   // row r = c/8 (key k_row_key(r)), slot c%8, holding chunk k_slot(r, c%8); of V, column c/4, slot c%4.
   int kvoff0, kvoff1, vvoff0, vvoff1;
@@ -432,7 +448,8 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) st.o[dt][i] = 0.f;
-  st.T = 0.f;
+  st.nT = 0.f;
+  st.nTL = -CB_LOG2_448;
   st.lsum = 0.f;
 
   // Tile it of the workgroup's key range is full for this wave when 64(it+1) <= e_w, half (first
@@ -518,7 +535,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(P.out) + o) = make_float4(r[0], r[1], r[2], r[3]);
         }
       }
-    if (hf == 0 && P.lse_out) P.lse_out[bhq * S + qr] = (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
+    if (hf == 0 && P.lse_out) P.lse_out[bhq * S + qr] = (log2f(lc_tot) - st.nT) * 0.69314718055994530942f;
     return;
   } else if (!kFused) {
     if (!wave_valid) return;
@@ -533,7 +550,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
                                        st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv);
         *reinterpret_cast<float4*>(orow + 32 * dt + 8 * g + 4 * hf) = val;
       }
-    if (hf == 0) P.lse_c[bhq * S + qr] = empty ? -INFINITY : (st.T + log2f(lc_tot)) * 0.69314718055994530942f;
+    if (hf == 0) P.lse_c[bhq * S + qr] = empty ? -INFINITY : (log2f(lc_tot) - st.nT) * 0.69314718055994530942f;
     return;
   } else {
     // ---- own block: keys qw .. qw+31, query qw + c sees keys up to itself ----------------------
@@ -601,7 +618,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
     swap32f(lo, lo2);
     lo += lo2;
     // ---- merge weights through the log-sum-exps (log2 units) ----------------------------------
-    const float l2c = empty ? -INFINITY : st.T + log2f(lc_tot);
+    const float l2c = empty ? -INFINITY : log2f(lc_tot) - st.nT;
     const float l2o = mo + log2f(lo);
     const float M = fmaxf(l2c, l2o);
     const float wc = empty ? 0.f : __builtin_amdgcn_exp2f(l2c - M);

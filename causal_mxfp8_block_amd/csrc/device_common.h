@@ -45,15 +45,6 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
-// Same with a power-of-two divisor applied by the conversion: codes of x / 2^k where `scale` is
-// 2^k as fp32 (only its exponent is used by the hardware).
-__device__ __forceinline__ uint32_t pack4_e4m3_scaled(float a, float b, float c, float d, float scale) {
-  v2s w = {0, 0};
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, scale, false);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, scale, true);
-  return (uint32_t)(uint16_t)w[0] | ((uint32_t)(uint16_t)w[1] << 16);
-}
-
 // E4M3 code -> fp32 value (exact), from the bit layout: exponent 0 is subnormal (m * 2^-9).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t e = (c >> 3) & 15u, m = c & 7u;

@@ -56,10 +56,11 @@ def _load():
                                                 P, P, P, P, P, P]
         lib.orc_quantize_v.argtypes = [P, I, I, I, I, I64, I64, I64, P, P, P, P]
         six = [P] * 6
-        lib.orc_attn_completed.argtypes = six + [I, I, I, I, I, F, P, I, I, P, P, D, P, P, D, ctypes.c_uint64]
+        lib.orc_attn_completed.argtypes = six + [I, I, I, I, I, F, P, I, I, P, P, D, P, P, P, P, D, ctypes.c_uint64]
         lib.orc_attn_own.argtypes = six + [I, I, I, I, I, F, P, I, P, P, D, P, P, D, ctypes.c_uint64]
-        lib.orc_attn_leaky.argtypes = six + [I, I, I, I, I, F, P, I, P, P, D, P, P, D, ctypes.c_uint64]
+        lib.orc_attn_leaky.argtypes = six + [I, I, I, I, I, F, P, I, P, P, D, P, P, P, P, D, ctypes.c_uint64]
         lib.orc_lse_merge.argtypes = [P, P, P, P, I64, I, P, P]
+        lib.orc_score_bound.argtypes = [P, P, P, P, I64, I64, P]
         raw = [P, I64, I64, I64] * 3
         lib.orc_attn_reference.argtypes = raw + [I, I, I, I, I, F, P, I, P, P]
         lib.orc_attn_identity.argtypes = raw + [I, I, I, I, I, F, P, I, P, P]
@@ -181,38 +182,64 @@ def _out(B, Hq, n, D):
     return np.empty((B, Hq, n, D), np.float64), np.empty((B, Hq, n), np.float64)
 
 
-# Bound of a kernel's score error per 64-wide block-scaled FP8 product step, as a multiple of the
-# step's largest |q.k| product (reading R15). The gfx950 MFMA measured at most 2^-12.56 on 131072
-# N(0,1) scores and 2^-11.6 on random full-range E4M3 codes; 2^-11 keeps a margin over both.
-SCORE_ERR = 2.0 ** -11
+# Multiplier of the hardware error model of reading R15 (1: the gfx950 block-scaled FP8 MFMA as the
+# probe tests measured it; 0: no hardware error, fp32 evaluation only).
+HW_ERR = 1.0
 
 
-def attn_completed(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None, t_shift=0, allowance=False,
-                   score_err=SCORE_ERR, jitter=0.0, jitter_seed=0):
-    """O7: completed-block partial (O_c [B,Hq,n,D], lse_c [B,Hq,n]) from codes in the ABI layouts.
+def score_bound(ac, as_, bc, bs) -> np.ndarray:
+    """Reading R15: bound [na, nb] of |hardware score - exact a.b| on the block-scaled FP8 MFMA for
+    rows of codes ac [na,128] / scale bytes as_ [na,4] against bc [nb,128] / bs [nb,4]."""
+    ac, as_, bc, bs = (np.ascontiguousarray(x, dtype=np.uint8) for x in (ac, as_, bc, bs))
+    out = np.empty((ac.shape[0], bc.shape[0]))
+    _load().orc_score_bound(_ptr(ac), _ptr(as_), _ptr(bc), _ptr(bs), ac.shape[0], bc.shape[0], _ptr(out))
+    return out
 
-    With ``allowance`` also returns the R15 allowance [B,Hq,n,D] (the largest change of O_c that the
-    hardware's dot-product error can make: alternative valid P codes, the normaliser, P.V
-    accumulation) and the bound of the lse error [B,Hq,n], for a score error of ``score_err`` per
-    product step. ``jitter`` (test model of a kernel) moves each score by up to ``jitter`` times its
-    bound."""
+
+@dataclass
+class Allowance:
+    """Reading R15 per output element [B,Hq,n,D]: ``total``, the largest change a kernel on the
+    block-scaled FP8 MFMA can make; ``code``, its term (i), alternative valid P codes; ``pv``, its
+    term (iii), the P.V products the MFMA cuts (the rest is the normaliser, own-block and
+    merge-weight terms); and ``lse_err`` [B,Hq,n], the bound of the lse error."""
+    total: np.ndarray
+    code: np.ndarray
+    pv: np.ndarray
+    lse_err: np.ndarray
+
+
+def _completed_like(fn, qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows, allowance, hw_err, jitter, jitter_seed,
+                    t_shift=None):
     B, _, S, D = qc.shape
     r, n = _rows_arg(rows, S)
     o, lse = _out(B, Hq, n, D)
-    al = np.empty_like(o) if allowance else None
+    al, ac, ap = ((np.empty_like(o) for _ in range(3)) if allowance else (None, None, None))
     le = np.empty_like(lse) if allowance else None
     args = [np.ascontiguousarray(a) for a in (qc, qs, kc, ks, vc, vcs)]
-    _load().orc_attn_completed(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, int(t_shift),
-                               _ptr(o), _ptr(lse), float(score_err), _ptr(al), _ptr(le), float(jitter),
-                               int(jitter_seed))
-    return (o, lse, al, le) if allowance else (o, lse)
+    extra = [] if t_shift is None else [int(t_shift)]
+    fn(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, *extra, _ptr(o), _ptr(lse),
+       float(hw_err), _ptr(al), _ptr(ac), _ptr(ap), _ptr(le), float(jitter), int(jitter_seed))
+    return (o, lse, Allowance(al, ac, ap, le)) if allowance else (o, lse)
 
 
-def attn_own(qc, qs, kc, ks, vt, vta, Hq, Hkv, scale, rows=None, allowance=False, score_err=SCORE_ERR, jitter=0.0,
+def attn_completed(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None, t_shift=0, allowance=False,
+                   hw_err=HW_ERR, jitter=0.0, jitter_seed=0):
+    """O7: completed-block partial (O_c [B,Hq,n,D], lse_c [B,Hq,n]) from codes in the ABI layouts.
+
+    With ``allowance`` also returns the R15 Allowance (the largest change of O_c that a kernel on the
+    block-scaled FP8 MFMA can make through the hardware's dot-product error and fp32 evaluation:
+    (i) alternative valid P codes, (ii) the normaliser, (iii) P.V accumulation), for ``hw_err``
+    times the measured error model (0 leaves fp32 evaluation only). ``jitter`` (test model of a
+    kernel) moves each score by up to ``jitter`` times its bound."""
+    return _completed_like(_load().orc_attn_completed, qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows, allowance,
+                           hw_err, jitter, jitter_seed, t_shift=t_shift)
+
+
+def attn_own(qc, qs, kc, ks, vt, vta, Hq, Hkv, scale, rows=None, allowance=False, hw_err=HW_ERR, jitter=0.0,
              jitter_seed=0):
     """O8: own-block partial (O_o, lse_o) on the token-normalised V. With ``allowance`` also the R15
-    allowance and lse error bound for a kernel whose own-block scores carry the hardware
-    dot-product error."""
+    Allowance for a kernel whose own-block scores carry the hardware dot-product error (no code or
+    P.V term: P is not quantised there)."""
     B, _, S, D = qc.shape
     r, n = _rows_arg(rows, S)
     o, lse = _out(B, Hq, n, D)
@@ -220,23 +247,18 @@ def attn_own(qc, qs, kc, ks, vt, vta, Hq, Hkv, scale, rows=None, allowance=False
     le = np.empty_like(lse) if allowance else None
     args = [np.ascontiguousarray(a) for a in (qc, qs, kc, ks, vt, vta)]
     _load().orc_attn_own(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, _ptr(o), _ptr(lse),
-                         float(score_err), _ptr(al), _ptr(le), float(jitter), int(jitter_seed))
-    return (o, lse, al, le) if allowance else (o, lse)
+                         float(hw_err), _ptr(al), _ptr(le), float(jitter), int(jitter_seed))
+    if not allowance:
+        return o, lse
+    return o, lse, Allowance(al, np.zeros_like(al), np.zeros_like(al), le)
 
 
-def attn_leaky(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None, allowance=False, score_err=SCORE_ERR, jitter=0.0,
+def attn_leaky(qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows=None, allowance=False, hw_err=HW_ERR, jitter=0.0,
                jitter_seed=0):
     """Ordinary causal MXFP8 (keys j <= i through the completed-block machinery, the last P block
-    partial). ``allowance``, ``score_err``, ``jitter``: as for attn_completed."""
-    B, _, S, D = qc.shape
-    r, n = _rows_arg(rows, S)
-    o, lse = _out(B, Hq, n, D)
-    al = np.empty_like(o) if allowance else None
-    le = np.empty_like(lse) if allowance else None
-    args = [np.ascontiguousarray(a) for a in (qc, qs, kc, ks, vc, vcs)]
-    _load().orc_attn_leaky(*[_ptr(a) for a in args], B, S, Hq, Hkv, D, float(scale), _ptr(r), n, _ptr(o), _ptr(lse),
-                           float(score_err), _ptr(al), _ptr(le), float(jitter), int(jitter_seed))
-    return (o, lse, al, le) if allowance else (o, lse)
+    partial). ``allowance``, ``hw_err``, ``jitter``: as for attn_completed."""
+    return _completed_like(_load().orc_attn_leaky, qc, qs, kc, ks, vc, vcs, Hq, Hkv, scale, rows, allowance, hw_err,
+                           jitter, jitter_seed)
 
 
 def lse_merge(oc, lsec, oo, lseo):
@@ -288,26 +310,29 @@ def quantize_all(q, k, v) -> Quantized:
     return Quantized(qc, qs, kc, ks, vc, vcs, vt, vta)
 
 
-def forward(q, k, v, scale, rows=None, quant: Quantized | None = None, score_err=SCORE_ERR):
+def forward(q, k, v, scale, rows=None, quant: Quantized | None = None, hw_err=HW_ERR):
     """The leak-free forward: quantise, completed partial, own partial, merge. Returns
-    (O [B,Hq,n,D], lse [B,Hq,n], parts) where parts holds the partials, the quantised operands and
+    (O [B,Hq,n,D], lse [B,Hq,n], parts) where parts holds the partials, the quantised operands,
     "allowance": the R15 allowance of the merged output, i.e. each partial's allowance times its
     merge weight w = e^(lse_part - lse), plus the first-order effect of the partials' lse errors on
-    the weights, w_c w_o |O_c - O_o| (err_c + err_o)."""
+    the weights, w_c w_o |O_c - O_o| (err_c + err_o); "allowance_code" and "allowance_pv", its terms
+    (i) (the alternative valid P codes of the completed partial) and (iii) (the P.V products the MFMA
+    cuts), times w_c."""
     qv, kv = _as_view(q), _as_view(k)
     Hq, Hkv = qv.H, kv.H
     z = quant if quant is not None else quantize_all(q, k, v)
-    oc, lc, alc, ec = attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, Hq, Hkv, scale, rows, allowance=True,
-                                     score_err=score_err)
-    oo, lo, alo, eo = attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, Hq, Hkv, scale, rows, allowance=True,
-                               score_err=score_err)
+    oc, lc, ac = attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, Hq, Hkv, scale, rows, allowance=True,
+                                hw_err=hw_err)
+    oo, lo, ao = attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, Hq, Hkv, scale, rows, allowance=True, hw_err=hw_err)
     o, lse = lse_merge(oc, lc, oo, lo)
     with np.errstate(invalid="ignore"):
         wc = np.where(np.isneginf(lc), 0.0, np.exp(lc - lse))
     wo = np.exp(lo - lse)
-    al = wc[..., None] * alc + wo[..., None] * alo + (wc * wo * (ec + eo))[..., None] * np.abs(oc - oo)
-    return o, lse, {"o_c": oc, "lse_c": lc, "o_o": oo, "lse_o": lo, "quant": z, "allowance_c": alc,
-                    "allowance_o": alo, "allowance": al, "lse_err": wc * ec + wo * eo}
+    ec, eo = ac.lse_err, ao.lse_err
+    al = wc[..., None] * ac.total + wo[..., None] * ao.total + (wc * wo * (ec + eo))[..., None] * np.abs(oc - oo)
+    return o, lse, {"o_c": oc, "lse_c": lc, "o_o": oo, "lse_o": lo, "quant": z, "allowance_c": ac.total,
+                    "allowance_o": ao.total, "allowance": al, "allowance_code": wc[..., None] * ac.code,
+                    "allowance_pv": wc[..., None] * ac.pv, "lse_err": wc * ec + wo * eo}
 
 
 def forward_leaky(q, k, v, scale, rows=None, quant: Quantized | None = None, allowance=False):

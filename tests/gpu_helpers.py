@@ -83,3 +83,50 @@ def report(name, got, ref, rms, rows=None, allowance=None, tol=None, k=5):
         say(f"    at (b, h, row, d) = ({idx[0]}, {idx[1]}, {row}, {idx[-1] if len(idx) > 3 else '-'}): "
             f"got {got[idx]:.6e} ref {ref[idx]:.6e} allowance {al[idx]:.3e}")
     return gated
+
+
+def gate(name, got, ref, rms, rows=None, allowance=None, allowance_hw=None, tol=2e-2, max_over_frac=None,
+         max_rms_err=1e-2, k=5):
+    """The forward parity gate, with what the R15 allowance absorbs made explicit. Asserts and prints.
+
+    err = |got - ref|, plain tolerance tol * rms (the stated bound max|err| <= tol * RMS).
+    ``allowance`` is the oracle's whole R15 allowance per element; ``allowance_hw`` its hardware
+    terms: (i) the change alternative valid P codes of the completed blocks can make and (iii) the
+    P.V products the block-scaled MFMA cuts (its measured arithmetic, pinned by the probe tests).
+    The rest is the normaliser, own-block and merge-weight terms, of the size of the score error
+    bound times |O|.
+      (a) every element: err <= tol * rms + allowance;
+      (b) every element with err > tol * rms has a nonzero hardware term, and its excess over the
+          plain tolerance and the other terms lies within the hardware terms;
+      (c) the fraction of elements with err > tol * rms is at most ``max_over_frac``;
+      (d) rms(err) <= max_rms_err * rms.
+    Prints the raw max|err| / rms, rms(err) / rms, the count over the plain tolerance and the
+    largest share of the hardware terms such an element needs. Returns those figures."""
+    err = np.abs(got - ref)
+    al = np.zeros_like(err) if allowance is None else allowance
+    hw = np.zeros_like(err) if allowance_hw is None else allowance_hw
+    rest = al - hw
+    plain = tol * rms
+    over = err > plain
+    n_over = int(over.sum())
+    need = np.where(over & (hw > 0), (err - plain - rest) / np.where(hw > 0, hw, 1.0), 0.0)
+    stats = dict(max_err=float(err.max() / rms), rms_err=float(np.sqrt(np.mean(err ** 2)) / rms), n_over=n_over,
+                 n=int(err.size), frac_over=n_over / err.size, gated=float((err - al).max() / rms),
+                 hw_share=float(need.max()) if n_over else 0.0)
+    say(f"[{name}] max|err|/rms = {stats['max_err']:.3e}  rms(err)/rms = {stats['rms_err']:.3e}  "
+        f"over {tol:g}*rms: {n_over} of {err.size} ({stats['frac_over']:.2e})  "
+        f"max(|err|-allowance)/rms = {stats['gated']:.3e}  largest hardware-term share used = {stats['hw_share']:.3f}  "
+        f"rms(ref) = {rms:.3e}")
+    worst = np.argsort((err - al).reshape(-1))[::-1][:k]
+    for w in worst:
+        idx = np.unravel_index(w, err.shape)
+        row = rows[idx[2]] if rows is not None and len(idx) > 2 else (idx[2] if len(idx) > 2 else None)
+        say(f"    at (b, h, row, d) = ({idx[0]}, {idx[1]}, {row}, {idx[-1] if len(idx) > 3 else '-'}): "
+            f"got {got[idx]:.6e} ref {ref[idx]:.6e} allowance {al[idx]:.3e} (hardware terms {hw[idx]:.3e})")
+    assert (err - al).max() <= plain, f"{name}: an element exceeds the tolerance plus the allowance"
+    assert np.all(hw[over] > 0), f"{name}: an element over the plain tolerance has no hardware term"
+    assert np.all(need <= 1.0 + 1e-9), f"{name}: an excess over the plain tolerance exceeds the hardware terms"
+    if max_over_frac is not None:
+        assert stats["frac_over"] <= max_over_frac, f"{name}: {n_over} elements over the plain tolerance"
+    assert stats["rms_err"] <= max_rms_err, f"{name}: rms(err) / rms = {stats['rms_err']:.3e}"
+    return stats

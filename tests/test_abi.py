@@ -187,3 +187,37 @@ def test_fused_bf16q_validation(args, status, needle):
                                                       a["vt"], FAKE, 1, S, Hq, 2, a["D"], 0.1, FAKE, S * Hq * 128,
                                                       Hq * 128, 128, a["dtype"], None, None))
     assert st == status and needle in msg, (st, msg)
+
+
+BIG_S = (1 << 24) + 32  # the first multiple of 32 above the largest supported length
+
+
+def test_sequence_length_bound_is_enforced():
+    """S > 2^24 is refused by every entry point that takes S, before any device work (the kernels
+    address a (b, head) slice of S * 128 code bytes with 32-bit offsets)."""
+    L = mx.lib()
+    S = BIG_S
+    st, msg = _err(L.mxfa_attn_fwd_completed_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, S, 4, 2, 128, 0.1, FAKE,
+                                                    FAKE, None))
+    assert st == 2 and "2^24" in msg, (st, msg)
+    st, msg = _err(L.mxfa_attn_fwd_own_block(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, S, 4, 2, 128, 0.1, FAKE, FAKE,
+                                             None))
+    assert st == 2 and "2^24" in msg, (st, msg)
+    st, msg = _err(L.mxfa_attn_fwd_fused_bf16q(FAKE, S * 512, 512, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, S, 4,
+                                               2, 128, 0.1, FAKE, S * 512, 512, 128, 0, None, None))
+    assert st == 2 and "2^24" in msg, (st, msg)
+    st, msg = _err(L.mxfa_attn_fwd_leaky(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, S, 4, 2, 128, 0.1, FAKE, S * 512, 512,
+                                         128, 0, None, None))
+    assert st == 2 and "2^24" in msg, (st, msg)
+    for mode in (0, 1):
+        st, msg = _err(L.mxfa_mxfp8_quantize(FAKE, 1, S, 2, 128, S * 256, 256, 128, mode, FAKE, FAKE,
+                                             FAKE if mode else None, FAKE if mode else None, None))
+        assert st == 2 and "2^24" in msg, (st, msg)
+    st, msg = _err(L.mxfa_lse_merge(FAKE, FAKE, FAKE, FAKE, 1, S, 2, 128, FAKE, S * 256, 256, 128, 0, None, None))
+    assert st == 2 and "2^24" in msg, (st, msg)
+    assert L.mxfa_attn_fwd_workspace_bytes(1, S, 4, 2, 128) == 0
+    assert L.mxfa_attn_bwd_workspace_bytes(1, S, 4, 2, 128) == 0
+    # the largest supported length itself passes the shape checks (and stops at the device check here)
+    st, msg = _err(L.mxfa_attn_fwd_completed_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1 << 24, 4, 2, 128, 0.1,
+                                                    FAKE, FAKE, None))
+    assert st != 2, msg

@@ -2,12 +2,15 @@
 whole forward) against the oracle, plus the causality invariant, determinism, poisoned outputs,
 layout and GQA identities on the HIP path.
 
-Tolerances: attention outputs max|err| <= 2e-2 * RMS(oracle output) (fp32 output mode); the
-RMS is that of the whole tensor, estimated from a seeded uniform sample of rows at full size. Where
-the oracle reports that a P code of the completed blocks lies within the hardware score error of a
-rounding boundary (reading R15: both codes are valid results), the element may in addition differ
-by the oracle's allowance, the largest change those alternative codes can make. The own-block
-partial and the merge carry no quantisation, only fp32 rounding: 1e-4 * RMS there."""
+Tolerance: attention outputs max|err| <= 2e-2 * RMS(oracle output) (fp32 output mode); the RMS is
+that of the whole tensor, estimated from a seeded uniform sample of rows at full size. The kernel
+forms its scores and P.V on the block-scaled FP8 MFMA, whose sums are not exact (reading R15): where
+a P value of the completed blocks lies within the hardware error bound of a rounding boundary both
+codes are valid results, and an element may in addition differ by the oracle's allowance. The gate
+(gpu_helpers.gate) keeps that allowance's terms apart: every element over the plain tolerance must
+have an alternative valid code in its row, the excess must fit the allowance, and at most 2e-3 of
+the elements may exceed the plain tolerance. The own-block partial and the merge carry no
+quantisation, only fp32 rounding: 1e-4 * RMS there."""
 import numpy as np
 import pytest
 import torch
@@ -15,11 +18,12 @@ import torch
 import oracle
 import causal_mxfp8_block_amd as mx
 from causal_mxfp8_block_amd.inputs import WORKLOADS, custom, make_inputs, perturb_after
-from gpu_helpers import (gpu_forward, gpu_quantize, oracle_view, report, sample_rows, say, to_dev,
+from gpu_helpers import (gate, gpu_forward, gpu_quantize, oracle_view, report, sample_rows, say, to_dev,
                          uniform_rows)
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
+MAX_OVER = 2e-3  # largest fraction of elements allowed over the plain tolerance (code flips)
 
 
 def _oracle_quant(inp):
@@ -35,8 +39,8 @@ def _partials_case(inp, rows=None):
     oc, lc = mx.attn_fwd_completed_blocks(g["qc"], g["qs"], g["kc"], g["ks"], g["vc"], g["vcs"], w.scale)
     oo, lo = mx.attn_fwd_own_block(g["qc"], g["qs"], g["kc"], g["ks"], g["vt"], g["vta"], w.scale)
     torch.cuda.synchronize()
-    roc, rlc, ral, _ = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale, rows,
-                                             allowance=True)
+    roc, rlc, ral = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale, rows,
+                                          allowance=True)
     roo, rlo = oracle.attn_own(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, w.Hq, w.Hkv, w.scale, rows)
     sel = slice(None) if rows is None else rows
     goc = oc.double().cpu().numpy()[:, :, sel]
@@ -60,7 +64,8 @@ def test_partials_small(shape):
     assert np.all(goc[:, :, :n0] == 0) and np.all(np.isneginf(glc[:, :, :n0]))
     if S > 32:
         rms = np.sqrt(np.mean(roc[:, :, 32:] ** 2))
-        assert report("o_c", goc[:, :, 32:], roc[:, :, 32:], rms, allowance=ral[:, :, 32:], tol=TOL) <= TOL
+        gate("o_c", goc[:, :, 32:], roc[:, :, 32:], rms, allowance=ral.total[:, :, 32:],
+             allowance_hw=ral.code[:, :, 32:] + ral.pv[:, :, 32:], tol=TOL, max_over_frac=MAX_OVER)
         assert np.max(np.abs(glc[:, :, 32:] - rlc[:, :, 32:])) < 1e-4
     rms_o = np.sqrt(np.mean(roo ** 2))
     assert report("o_o", goo, roo, rms_o) <= 1e-4
@@ -110,9 +115,33 @@ def test_forward_parity_workloads(name):
                                   rms_rows, quant=z)
         rms = np.sqrt(np.mean(ru ** 2))
     sel = slice(None) if rows is None else rows
-    ratio = report(f"forward {name}", go[:, :, sel], ro, rms, rows, allowance=parts["allowance"], tol=TOL)
+    gate(f"forward {name}", go[:, :, sel], ro, rms, rows, allowance=parts["allowance"],
+         allowance_hw=parts["allowance_code"] + parts["allowance_pv"], tol=TOL, max_over_frac=MAX_OVER)
     assert np.max(np.abs(gl[:, :, sel] - rl)) < 1e-3
-    assert ratio <= TOL
+
+
+def test_completed_partial_full_size():
+    """The completed-block kernel alone (attn_fwd_completed_blocks) at the benchmark workload's full
+    size, on sampled rows of every head, against the oracle's completed partial."""
+    inp = make_inputs("gqa16x4_s32k_amplitudes")
+    w = inp.workload
+    say(f"completed partial at full size: {w.name}")
+    g = gpu_quantize(inp)
+    oc, lc = mx.attn_fwd_completed_blocks(g["qc"], g["qs"], g["kc"], g["ks"], g["vc"], g["vcs"], w.scale)
+    torch.cuda.synchronize()
+    z = _oracle_quant(inp)
+    rows = sample_rows(w.S, w.seed)
+    rows = rows[rows >= 32]
+    roc, rlc, ral = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale, rows,
+                                          allowance=True)
+    ru, _ = oracle.attn_completed(z.qc, z.qs, z.kc, z.ks, z.vc, z.vcs, w.Hq, w.Hkv, w.scale,
+                                  uniform_rows(w.S, w.seed)[uniform_rows(w.S, w.seed) >= 32])
+    rms = np.sqrt(np.mean(ru ** 2))
+    goc = oc.double().cpu().numpy()[:, :, rows]
+    glc = lc.double().cpu().numpy()[:, :, rows]
+    gate("completed full size", goc, roc, rms, rows, allowance=ral.total, allowance_hw=ral.code + ral.pv, tol=TOL,
+         max_over_frac=MAX_OVER)
+    assert np.max(np.abs(glc - rlc)) < 1e-3
 
 
 def test_bf16_output_is_rne_of_f32_output():
@@ -144,7 +173,8 @@ def test_fused_entry_equals_attn_fwd_and_stepwise_path_matches_oracle():
     rms = np.sqrt(np.mean(ro ** 2))
     for name, o_, l_ in (("fused", of, lf), ("stepwise", o2, l2)):
         go = o_.double().cpu().numpy().transpose(0, 2, 1, 3)
-        assert report(name, go, ro, rms, allowance=parts["allowance"], tol=TOL) <= TOL
+        gate(name, go, ro, rms, allowance=parts["allowance"],
+             allowance_hw=parts["allowance_code"] + parts["allowance_pv"], tol=TOL, max_over_frac=MAX_OVER)
         assert np.max(np.abs(l_.double().cpu().numpy() - rl)) < 1e-3
 
 
@@ -187,18 +217,23 @@ def test_causality_every_t_tiny():
 
 
 @pytest.mark.parametrize("name,ts", [("gqa16x4_s8k_outliers", [31, 32, 33, 4095, 8159, 8190]),
-                                     ("gqa16x4_s32k_amplitudes", [40, 16383, 32700])])
+                                     ("mha16_s16k", [63, 8200, 16350]),
+                                     ("gqa16x4_s32k_amplitudes", [40, 16383, 32700]),
+                                     ("mha16_s32k_sbhd", [100, 20000, 32740])])
 def test_causality_workloads(name, ts):
     inp = make_inputs(name)
     lay = inp.workload.layout
     q, k, v = (to_dev(getattr(inp, n)) for n in ("q", "k", "v"))
     o0, l0 = mx.attn_fwd(q, k, v, layout=lay, out_dtype=torch.float32)
+    rows = (lambda o, t: o[:, :t + 1]) if lay == "bshd" else (lambda o, t: o[:t + 1])
     for t in ts:
         say(f"causality {name} t={t}")
         p = perturb_after(inp, t, outlier_at_next=True)
         o1, l1 = mx.attn_fwd(to_dev(p.q), to_dev(p.k), to_dev(p.v), layout=lay, out_dtype=torch.float32)
-        assert torch.equal(o0[:, :t + 1], o1[:, :t + 1]), t
+        assert torch.equal(rows(o0, t), rows(o1, t)), t
         assert torch.equal(l0[:, :, :t + 1], l1[:, :, :t + 1]), t
+        # and the rows after t did change (the perturbation reached the kernel)
+        assert not torch.equal(o0, o1), t
 
 
 def test_deterministic_and_poison_overwritten():

@@ -2,8 +2,10 @@
 variant, and the leak itself on the GPU: a later token of a query's own 32-token block changes that
 query's output here, while the leak-free forward stays bit-identical.
 
-Tolerance: as for the leak-free forward, max(|err| - allowance) <= 2e-2 * RMS(oracle output), with
-the oracle's R15 allowance (several valid P codes under the hardware's score error)."""
+Tolerance: as for the leak-free forward (gpu_helpers.gate): max|err| <= 2e-2 * RMS(oracle output)
+except where the oracle's R15 allowance names an alternative valid P code under the hardware's
+error bound, the excess within the allowance, at most 2e-3 of the elements over the plain
+tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -11,10 +13,11 @@ import torch
 import oracle
 import causal_mxfp8_block_amd as mx
 from causal_mxfp8_block_amd.inputs import custom, make_inputs, perturb_after
-from gpu_helpers import gpu_forward, gpu_quantize, oracle_view, report, sample_rows, say, uniform_rows
+from gpu_helpers import gate, gpu_forward, gpu_quantize, oracle_view, sample_rows, say, uniform_rows
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
+MAX_OVER = 2e-3
 
 
 def _gpu_leaky(inp, out_dtype=torch.float32):
@@ -43,9 +46,9 @@ def test_leaky_matches_oracle_small(shape):
     inp = make_inputs(custom(B, Hq, Hkv, S, values="outliers", seed=100 + sum(shape)))
     say(f"leaky {shape}")
     go, gl, _ = _gpu_leaky(inp)
-    ro, rl, al, _ = _oracle_leaky(inp)
+    ro, rl, A = _oracle_leaky(inp)
     rms = np.sqrt(np.mean(ro ** 2))
-    assert report("leaky", go, ro, rms, allowance=al, tol=TOL) <= TOL
+    gate("leaky", go, ro, rms, allowance=A.total, allowance_hw=A.code + A.pv, tol=TOL, max_over_frac=MAX_OVER)
     assert np.max(np.abs(gl - rl)) < 1e-3
 
 
@@ -56,10 +59,11 @@ def test_leaky_matches_oracle_workloads(name):
     say(f"leaky {name}")
     go, gl, _ = _gpu_leaky(inp)
     rows = sample_rows(w.S, w.seed)
-    ro, rl, al, _ = _oracle_leaky(inp, rows)
-    ru, _, _, _ = _oracle_leaky(inp, uniform_rows(w.S, w.seed))
+    ro, rl, A = _oracle_leaky(inp, rows)
+    ru = _oracle_leaky(inp, uniform_rows(w.S, w.seed))[0]
     rms = np.sqrt(np.mean(ru ** 2))
-    assert report(f"leaky {name}", go[:, :, rows], ro, rms, rows, allowance=al, tol=TOL) <= TOL
+    gate(f"leaky {name}", go[:, :, rows], ro, rms, rows, allowance=A.total, allowance_hw=A.code + A.pv, tol=TOL,
+         max_over_frac=MAX_OVER)
     assert np.max(np.abs(gl[:, :, rows] - rl)) < 1e-3
 
 
