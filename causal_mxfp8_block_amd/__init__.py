@@ -22,6 +22,7 @@ _lib = None
 
 ROWWISE, V = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
+NOALLOC_WORKSPACE_BYTES = 256 << 20  # MXFA_NOALLOC_WORKSPACE_BYTES of include/mxfa.h
 
 
 class MxfaError(RuntimeError):
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.mxfa_attn_fwd_workspace_bytes.restype = SZ
         L.mxfa_attn_fwd.argtypes = [P, I64, I64, I64] * 3 + [I, I, I, I, I, F, P, SZ, P, I64, I64, I64, I, P, P]
         L.mxfa_attn_fwd.restype = I
+        L.mxfa_attn_fwd_noalloc.argtypes = [P, I64, I64, I64] * 3 + [I, I, I, I, I, F, P, I64, I64, I64, I, P, P]
+        L.mxfa_attn_fwd_noalloc.restype = I
         _lib = L
     return _lib
 
@@ -277,6 +280,26 @@ def attn_fwd(q, k, v, softmax_scale: float | None = None, layout: str = "bshd", 
     _check(lib().mxfa_attn_fwd(_p(q), qsb, qss, qsh, _p(k), ksb, kss, ksh, _p(v), vsb, vss, vsh, B, S, Hq, Hkv, D,
                                scale, _p(workspace), workspace.numel(), _p(out), osb, oss, osh,
                                _out_code(out.dtype), _p(lse), _stream(q)))
+    return out, lse
+
+
+def attn_fwd_noalloc(q, k, v, softmax_scale: float | None = None, layout: str = "bshd", out_dtype=torch.bfloat16,
+                     out=None, lse=None):
+    """attn_fwd through the entry point that allocates nothing (its workspace is the library's static
+    device array; calls that overlap on one device race). The outputs are allocated here unless
+    given; returns (out in q's layout, lse [B,Hq,S])."""
+    B, S, Hq, D, qsb, qss, qsh = view_of(q, layout)
+    _, _, Hkv, _, ksb, kss, ksh = view_of(k, layout)
+    _, _, _, _, vsb, vss, vsh = view_of(v, layout)
+    scale = default_scale(D) if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _, _, _, _, osb, oss, osh = view_of(out, layout)
+    _check(lib().mxfa_attn_fwd_noalloc(_p(q), qsb, qss, qsh, _p(k), ksb, kss, ksh, _p(v), vsb, vss, vsh, B, S, Hq,
+                                       Hkv, D, scale, _p(out), osb, oss, osh, _out_code(out.dtype), _p(lse),
+                                       _stream(q)))
     return out, lse
 
 

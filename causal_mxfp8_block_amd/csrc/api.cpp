@@ -377,6 +377,39 @@ MXFA_EXPORT int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t q
                     "fused attention");
 }
 
+MXFA_EXPORT int mxfa_attn_fwd_noalloc(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const void* k,
+                                      int64_t ksb, int64_t kss, int64_t ksh, const void* v, int64_t vsb, int64_t vss,
+                                      int64_t vsh, int B, int S, int Hq, int Hkv, int D, float softmax_scale,
+                                      void* out, int64_t osb, int64_t oss, int64_t osh, int out_dtype,
+                                      float* lse_out, void* stream) {
+  g_last_error.clear();
+  TRY(check_attn_shape(B, S, Hq, Hkv, D));
+  TRY(check_view("q", q, B, S, Hq, qsb, qss, qsh, 8));
+  TRY(check_view("k", k, B, S, Hkv, ksb, kss, ksh, 8));
+  TRY(check_view("v", v, B, S, Hkv, vsb, vss, vsh, 8));
+  if (out_dtype != MXFA_OUT_BF16 && out_dtype != MXFA_OUT_F32)
+    return fail(MXFA_ERR_UNSUPPORTED, "unknown output dtype %d", out_dtype);
+  TRY(check_view("out", out, B, S, Hq, osb, oss, osh, out_dtype == MXFA_OUT_BF16 ? 8 : 4));
+  if (lse_out && !aligned16(lse_out)) return fail(MXFA_ERR_ALIGN, "lse_out is not 16-byte aligned");
+  const size_t need = carve(nullptr, B, S, Hq, Hkv).bytes;
+  if (need > mxfa::kNoallocWorkspaceBytes)
+    return fail(MXFA_ERR_UNSUPPORTED, "B = %d, S = %d, Hkv = %d need %zu workspace bytes; the static workspace holds %zu",
+                B, S, Hkv, need, mxfa::kNoallocWorkspaceBytes);
+  TRY(check_device());
+  void* ws = nullptr;
+  TRY(hip_status(mxfa::noalloc_workspace(&ws), "static workspace address"));
+  const Workspace w = carve(ws, B, S, Hq, Hkv);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t *q16 = static_cast<const uint16_t*>(q), *k16 = static_cast<const uint16_t*>(k),
+                 *v16 = static_cast<const uint16_t*>(v);
+  TRY(hip_status(mxfa::launch_quantize_rowwise(k16, B, S, Hkv, ksb, kss, ksh, w.kc, w.ks, st), "quantize k"));
+  TRY(hip_status(mxfa::launch_quantize_v(v16, B, S, Hkv, vsb, vss, vsh, w.vc, w.vcs, w.vt, w.vta, st), "quantize v"));
+  return hip_status(mxfa::launch_attn_fused(nullptr, nullptr, w.kc, w.ks, w.vc, w.vcs, w.vt, w.vta, B, S, Hq, Hkv,
+                                           softmax_scale, out, osb, oss, osh, out_dtype == MXFA_OUT_BF16, lse_out,
+                                           st, nullptr, q16, qsb, qss, qsh),
+                    "fused attention");
+}
+
 MXFA_EXPORT size_t mxfa_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D) {
   if (D != 128 || B < 1 || S < 1 || S > kMaxS || Hq < 1 || Hkv < 1) return 0;
   return carve_bwd(nullptr, B, S, Hq, Hkv).bytes;

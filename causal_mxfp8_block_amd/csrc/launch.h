@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mxfa.h"
+
 namespace mxfa {
 
 // Workspace parts of the backward: decoded bf16 operands, head-major, and the transposed copies.
@@ -12,6 +14,12 @@ struct BwdWorkspace {
   float* lse2;                                      // lse * log2(e), [B,Hq,S]
   size_t bytes;
 };
+
+// Size of the static device workspace of mxfa_attn_fwd_noalloc (noalloc.hip), as the header states it:
+// 256 MiB, enough for the K and V encodings of B * Hkv * S <= 655360 (S = 32768 with 16 KV heads).
+constexpr size_t kNoallocWorkspaceBytes = MXFA_NOALLOC_WORKSPACE_BYTES;
+// That workspace's address on the current device (looked up once per device).
+hipError_t noalloc_workspace(void** ptr);
 
 hipError_t launch_quantize_rowwise(const uint16_t* x, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
                                    uint8_t* codes, uint8_t* scales, hipStream_t stream);

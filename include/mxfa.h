@@ -162,6 +162,24 @@ int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const vo
                   int D, float softmax_scale, void* workspace, size_t workspace_bytes, void* out, int64_t osb,
                   int64_t oss, int64_t osh, int out_dtype, float* lse_out, void* stream);
 
+/* attn_fwd_noalloc -- attn_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and result (bit for
+ * bit), with the K and V encodings in a static device workspace of the library instead of a
+ * caller-provided one. The call itself allocates nothing; the caller still passes q, k, v, out and
+ * lse_out. The workspace is a file-scope device array of MXFA_NOALLOC_WORKSPACE_BYTES (256 MiB) held
+ * on every device the library runs on until the process ends; its address is looked up on the first
+ * call on each device (when the HIP runtime backs the array; later calls touch no allocator). A
+ * problem needing more (mxfa_attn_fwd_workspace_bytes above it)
+ * is refused with MXFA_ERR_UNSUPPORTED before anything is enqueued. Every call on one device uses the
+ * same array, which keeps the last call's contents: calls that overlap on one device (different
+ * streams or threads without ordering between them) race and give undefined results. Arguments as
+ * attn_fwd, without the workspace. */
+#define MXFA_NOALLOC_WORKSPACE_BYTES ((size_t)256 << 20)
+int mxfa_attn_fwd_noalloc(const void* q, int64_t qsb, int64_t qss, int64_t qsh, const void* k, int64_t ksb,
+                          int64_t kss, int64_t ksh, const void* v, int64_t vsb, int64_t vss, int64_t vsh, int B, int S,
+                          int Hq, int Hkv, int D, float softmax_scale, void* out, int64_t osb, int64_t oss,
+                          int64_t osh, int out_dtype, float* lse_out, void* stream);
+
 /* Bytes of workspace mxfa_attn_bwd needs (decoded operands: 5 bf16 copies of [B,Hq,S,D] and 3 of
  * [B,Hkv,S,D], plus two [B,Hq,S] fp32 arrays; 256-byte aligned parts). */
 size_t mxfa_attn_bwd_workspace_bytes(int B, int S, int Hq, int Hkv, int D);

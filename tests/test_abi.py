@@ -221,3 +221,17 @@ def test_sequence_length_bound_is_enforced():
     st, msg = _err(L.mxfa_attn_fwd_completed_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1 << 24, 4, 2, 128, 0.1,
                                                     FAKE, FAKE, None))
     assert st != 2, msg
+
+
+def test_noalloc_refuses_oversized_problems_before_device_work():
+    """mxfa_attn_fwd_noalloc checks the problem against its static workspace on the host: a problem
+    needing more than MXFA_NOALLOC_WORKSPACE_BYTES of K/V encodings is refused, naming the limit."""
+    L = mx.lib()
+    S, Hkv = 65536, 16
+    assert L.mxfa_attn_fwd_workspace_bytes(1, S, 16, Hkv, 128) > mx.NOALLOC_WORKSPACE_BYTES
+    st, msg = _err(L.mxfa_attn_fwd_noalloc(FAKE, S * 2048, 2048, 128, FAKE, S * 2048, 2048, 128, FAKE, S * 2048, 2048,
+                                           128, 1, S, 16, Hkv, 128, 0.1, FAKE, S * 2048, 2048, 128, 0, None, None))
+    assert st == 3 and "static workspace" in msg, (st, msg)
+    with open(HEADER) as f:
+        assert f"MXFA_NOALLOC_WORKSPACE_BYTES ((size_t)256 << 20)" in f.read()
+    assert mx.NOALLOC_WORKSPACE_BYTES == 256 << 20
