@@ -64,5 +64,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PEAK_SRC = os.path.join(PKG, "peak", "mfma_peak.hip")
+PEAK_LIB = os.path.join(PKG, "libmxfa_peak.so")
+
+
+def build_peak() -> str:
+    """Compile the benchmark's MFMA throughput probe into causal_mxfp8_block_amd/libmxfa_peak.so."""
+    tmp = PEAK_LIB + f".tmp{os.getpid()}"
+    res = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", tmp, PEAK_SRC], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"mfma_peak build failed ({res.returncode}):\n{_clean(res.stderr)}")
+    os.replace(tmp, PEAK_LIB)
+    return PEAK_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
