@@ -11,8 +11,9 @@
 //  * A preparation pass decodes Q, K and V to bf16 (exact: an E4M3 value times a power of two has 4
 //    significant bits) and copies dO, each head-major, plus a transposed [D][S] copy of Q, K and dO
 //    for the MFMA operands that contract over tokens; it also forms Delta.
-//  * dK/dV kernel: one wave per 16 keys, two waves per SIMD, their K and V operands held in registers
-//    (16x16x32 MFMAs). For every query head of the KV head and every 32-query block at or after the
+//  * dK/dV kernel: one wave per 32 keys, one wave per SIMD (its 512 registers hold the K and V
+//    operands, both accumulators and a whole pipelined step). For every query head of the KV head and
+//    every 32-query block at or after the
 //    keys, it computes S = Q K^T and dP = dO V^T (keys on the lanes, queries on the accumulator
 //    elements), P and dS elementwise, and accumulates dV^T += dO^T P and dK^T += Q^T dS. P and dS stay
 //    in their accumulator registers and are the B operand of those MFMAs: the accumulator's query
@@ -53,11 +54,9 @@ __device__ __forceinline__ v8bf to_bf16(const v16f& x, int t) {
   return r;
 }
 
-// Position of query q (0..31) of a transposed dK/dV tile row: MFMA slot order, so that lane group g
-// reads queries 4g..4g+3 and 16+4g..16+4g+3 as one 16-byte operand (positions 8g..8g+7).
-__device__ __forceinline__ int dkdv_tpos(int q) { return 8 * ((q >> 2) & 3) + 4 * (q >> 4) + (q & 3); }
-// Same for the dQ kernel's 32x32 operands: within each 16-token half, bits 2 and 3 swapped, so that lane
-// half h reads tokens 4h..4h+3 and 8+4h..8+4h+3 of the half as one 16-byte operand.
+// Position of token q (0..31) of a transposed tile row in the MFMA slot order of both kernels'
+// 32x32x16 operands: within each 16-token half, bits 2 and 3 swapped, so that lane half h reads tokens
+// 4h..4h+3 and 8+4h..8+4h+3 of the half as one 16-byte operand (the accumulator's row order).
 __device__ __forceinline__ int dq_tpos(int q) { return (q & 16) | ((q & 4) << 1) | ((q & 8) >> 1) | (q & 3); }
 
 // ---- preparation -------------------------------------------------------------------------------
@@ -65,9 +64,8 @@ __device__ __forceinline__ int dq_tpos(int q) { return (q & 16) | ((q & 4) << 1)
 // 32(g%4) .. +32. Source kSrc: 0 rowwise codes + E8M0 per 32 columns, 1 token-normalised codes + one
 // E8M0 amplitude per token, 2 a bf16 [B,S,H,D] view (with Delta from the o view and lse * log2(e)
 // from lse when delta != null). Writes the bf16 rows to out [B,H,S,D] and, when out_t != null, the
-// transposed out_t [B,H,D,S]; with kSlot 1 (2) the tokens of each 32-token block of out_t are stored in
-// the dK/dV (dQ) kernel's MFMA slot order, dkdv_tpos (dq_tpos), so that its tiles load as contiguous
-// 16-byte pieces.
+// transposed out_t [B,H,D,S]; with kSlot 1 the tokens of each 32-token block of out_t are stored in the
+// MFMA slot order, dq_tpos, so that the tiles load as contiguous 16-byte pieces.
 template <int kSrc, int kSlot = 0>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, const uint8_t* scales, const uint16_t* x,
                                                        int64_t sb, int64_t ss, int64_t sh, const uint16_t* o,
@@ -144,7 +142,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* codes, con
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     // tokens t0 + 2e and t0 + 2e + 1 stay one dword (both orders keep even-odd pairs together)
-    const int pos = kSlot == 1 ? (dkdv_tpos(2 * e) >> 1) : kSlot == 2 ? (dq_tpos(2 * e) >> 1) : e;
+    const int pos = kSlot == 1 ? (dq_tpos(2 * e) >> 1) : e;
     p[pos] = (uint32_t)tile[(t0 + 2 * e) * BW_ROW + d] | ((uint32_t)tile[(t0 + 2 * e + 1) * BW_ROW + d] << 16);
   }
   uint4* tdst = reinterpret_cast<uint4*>(out_t + (bh * 128 + d) * S + s0 + t0);
@@ -156,19 +154,13 @@ struct BwdParams {
   const uint16_t *qd, *qdt, *kd, *kdt, *vd, *gd, *gdt;  // decoded operands (workspace)
   const float *lse, *delta;                              // [B,Hq,S]
   const float* lse2;                                     // lse * log2(e), [B,Hq,S] (workspace)
-  int S, Hq, Hkv;
+  int B, S, Hq, Hkv;
   float scale, scale_log2;
   uint16_t *dq, *dk, *dv;                                // bf16 outputs (views)
   int64_t qsb, qss, qsh, ksb, kss, ksh;                 // strides of dq and of dk/dv
 };
 
 // ---- dK, dV ------------------------------------------------------------------------------------
-// v_mfma_f32_16x16x32_bf16 (operand layout probed): A lane (m = l%16, g = l/16) element e <-> A[m][8g+e];
-// B lane (n = l%16, g) element e <-> B[8g+e][n]; C lane (n = l%16, g) element i <-> C[4g+i][n].
-typedef float v4f __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4f mfma16(const v8bf& a, const v8bf& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 // Global -> LDS without registers: lane l's 16 (or 4) bytes land at lds + 16 l (4 l); lds wave-uniform.
 __device__ __forceinline__ void gload_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g, (__attribute__((address_space(3))) void*)lds,
@@ -179,207 +171,328 @@ __device__ __forceinline__ void gload_lds4(const void* g, void* lds) {
                                    4, 0, 0);
 }
 
-// Workgroup: 8 waves (two per SIMD) = keys 128 kt .. 128 kt + 127 of (b, hk); wave w owns keys
-// 128 kt + 16 w + [0, 16), its K and V rows held in registers as B operands and its dK^T, dV^T
-// accumulators (128 x 16 each) in registers. Steps n = (query head, 32-query block), the blocks from
-// the last one down to 4kt: workgroups that run together read the same query block at the same time.
-// Per step, keys on the MFMA columns: S = Q K^T and dP = dO V^T (two 16-query row tiles, K = D in four
-// 32-wide steps), P and dS elementwise in the accumulators, then dV^T += dO^T P and dK^T += Q^T dS with
-// P and dS as the B operand straight from those accumulators (element i of row tile mt is query
-// 16mt + 4g + i: slot (g, e) of the contraction is query 16(e/4) + 4g + e%4, the order in which the
-// preparation pass stores the transposed copies). Each step's tiles go from global memory straight
-// into a ring of four LDS slots (loads with the LDS flag, no registers), two steps ahead. The loop is
-// software-pipelined: while the VALU computes P and dS of step st, the matrix core runs the S and dP
-// products of step st + 1 and the dV and dK products of step st - 1.
-constexpr int DKDV_NBUF = 4;  // LDS ring: steps st - 1, st, st + 1 and st + 2 (arriving)
-struct DkdvTiles {
-  // Unpadded rows; reads stay conflict-free through XOR swizzles of the 16-byte chunks:
-  uint16_t q[32 * 128], g[32 * 128];    // Q, dO rows: chunk c of row r in slot c ^ (r & 15)
-  uint16_t qt[128 * 32], gt[128 * 32];  // Q^T, dO^T rows (slot order): chunk c of row d in slot c ^ ((d >> 2) & 3)
-  float l[32], d[32];                   // lse * log2(e) and Delta of the step's 32 queries
-};
-// Step n_'s tiles from global memory straight into slot T (lane l's bytes at the wave's base + 16 l):
-// thread tid fills LDS chunk tid (16 bytes) of each of the four tiles: of Q and dO, row r = tid/16,
-// slot tid%16, holding chunk (tid%16) ^ (r & 15) of that query's row; of Q^T and dO^T, row d = tid/4,
-// slot tid%4, holding chunk (tid%4) ^ ((d >> 2) & 3) of the block's 64 bytes of row d. Wave 0 also
-// moves the 32 lse * log2(e) and 32 Delta values (4 bytes per lane).
-__device__ __forceinline__ void dkdv_fetch(const uint16_t* __restrict__ qd, const uint16_t* __restrict__ gd,
-                                           const uint16_t* __restrict__ qdt, const uint16_t* __restrict__ gdt,
-                                           const float* __restrict__ lse2, const float* __restrict__ delta,
-                                           DkdvTiles* __restrict__ T, int n_, int b, int hk, int G, int per_head,
-                                           int nqb, int S, int Hq, int rr, int rx, int td, int tx, int lane,
-                                           int wave_u) {
-  const int hq_ = hk * G + n_ / per_head, q0_ = 32 * (nqb - 1 - n_ % per_head);
-  const int64_t bhq_ = (int64_t)b * Hq + hq_;
-  gload_lds16(qd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T->q) + 1024 * wave_u);
-  gload_lds16(gd + (bhq_ * S + q0_ + rr) * 128 + 8 * rx, reinterpret_cast<uint8_t*>(T->g) + 1024 * wave_u);
-  gload_lds16(qdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T->qt) + 1024 * wave_u);
-  gload_lds16(gdt + (bhq_ * 128 + td) * S + q0_ + 8 * tx, reinterpret_cast<uint8_t*>(T->gt) + 1024 * wave_u);
-  if (wave_u == 0) gload_lds4(lane < 32 ? lse2 + bhq_ * S + q0_ + lane : delta + bhq_ * S + q0_ + lane - 32, T->l);
+// The same loads written out, for loops that keep several iterations' loads in flight: the compiler
+// does not see them, so it neither counts them in its waits nor makes every LDS read wait for them (it
+// cannot tell the slots apart across iterations); the loop waits for them itself. Address = a scalar
+// base plus a 32-bit per-lane byte offset; M0 holds the LDS address, set by the compiler through the
+// operand constraint; the nop is the wait state an LDS DMA needs after an M0 write. No register is
+// written, so nothing of the instruction stays in flight in a register.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma_lds16(const void* base, uint32_t voff, void* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
+}
+__device__ __forceinline__ void dma_lds4(const void* base, uint32_t voff, void* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
 }
 
-// One iteration of the pipelined dK/dV loop: step st + 2's loads into slot L; the S and dP MFMAs of
-// step st + 1 (tiles Tn, into sn, pn) and the dV and dK MFMAs of step st - 1 (tiles Tp, with its P
-// and dS in pbp, sbp), one of each per group, interleaved with P and dS of step st (scores in sc, pc;
-// lse and Delta from Tc). The slots and the global sources are restrict pointers: L is none of Tc,
-// Tn, Tp, so the compiler can tell the LDS reads from the loads in flight and does not wait for
-// those loads before the reads. Past the last step Tn is a stale slot (its products are unused).
-__device__ __forceinline__ void dkdv_pipe_iter(
-    const uint16_t* __restrict__ qd, const uint16_t* __restrict__ gd, const uint16_t* __restrict__ qdt,
-    const uint16_t* __restrict__ gdt, const float* __restrict__ lse2, const float* __restrict__ delta,
-    const DkdvTiles* __restrict__ Tc, const DkdvTiles* __restrict__ Tn, const DkdvTiles* __restrict__ Tp,
-    DkdvTiles* __restrict__ L, int st, int nsteps, int b, int hk, int G, int per_head, int nqb, int S, int Hq, int rr,
-    int rx, int td, int tx, int lane, int wave_u, int n, int g, int key0, float scale_log2, const v8bf (&kop)[4],
-    const v8bf (&vop)[4], v4f (&dkT)[8], v4f (&dvT)[8], v4f (&sc)[2], v4f (&pc)[2], v4f (&sn)[2], v4f (&pn)[2],
-    v8bf& pbp, v8bf& sbp) {
-  if (st + 2 < nsteps)
-    dkdv_fetch(qd, gd, qdt, gdt, lse2, delta, L, st + 2, b, hk, G, per_head, nqb, S, Hq, rr, rx, td, tx, lane, wave_u);
-  const int qb = nqb - 1 - st % per_head;
-  const int koff = key0 - 32 * qb;  // key - query offset of the two blocks' first tokens
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sn[mt][i] = pn[mt][i] = 0.f;
-  float lv[8], dv[8];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const float4 l4 = *reinterpret_cast<const float4*>(Tc->l + 16 * mt + 4 * g);
-    const float4 d4 = *reinterpret_cast<const float4*>(Tc->d + 16 * mt + 4 * g);
-    lv[4 * mt] = l4.x; lv[4 * mt + 1] = l4.y; lv[4 * mt + 2] = l4.z; lv[4 * mt + 3] = l4.w;
-    dv[4 * mt] = d4.x; dv[4 * mt + 1] = d4.y; dv[4 * mt + 2] = d4.z; dv[4 * mt + 3] = d4.w;
+// Workgroup: 4 waves, one per SIMD, = keys 128 kt .. 128 kt + 127 of (b, hk); wave w owns keys
+// 128 kt + 32 w + [0, 32), its K and V rows held in registers as B operands and its dK^T and dV^T
+// accumulators (128 x 32 each) in registers. 32 keys per wave let every Q and dO element read from LDS
+// feed 32 keys of each product, half the LDS traffic per FLOP of a 16-key wave. Steps n = (query head,
+// 32-query block), the blocks from the last one down to 4kt. Per step, with the keys on the MFMA
+// columns (v_mfma_f32_32x32x16_bf16: A lane (m = l%32, g = l/32) element e <-> A[m][8g+e]; B lane
+// (n = l%32, g) element e <-> B[8g+e][n]; C lane (n, g) element i <-> C[8(i/4) + 4g + i%4][n]):
+// S = Q K^T and dP = dO V^T (K = D in eight 16-wide steps), P and dS elementwise in the accumulators
+// (lane: key l%32, element i: query 8(i/4) + 4g + i%4), then dV^T += dO^T P and dK^T += Q^T dS, two
+// 16-query slices each, with P and dS as the B operand straight from the accumulators: slot (g, e) of
+// slice t is accumulator element 8t + e, query 16t + 8(e/4) + 4g + e%4 (dq_tpos, the order in which
+// the preparation pass stores the transposed copies). The loop is software-pipelined: in iteration i
+// the VALU computes P and dS of step i while the matrix core runs the S and dP products of step i + 1
+// and the dV and dK products of step i - 1. The tiles go from global memory straight into LDS (loads
+// with the LDS flag) in three rings, each as far ahead as its slots allow: the Q and dO rows of step
+// i + 4 (read in iteration i + 3), the transposed tiles of step i + 2 (read in iteration i + 3) and the
+// lse and Delta of step i + 3 (read in iteration i + 3); so every load has two iterations to arrive,
+// and an iteration ends by waiting only for the loads issued two iterations before. Every iteration
+// issues the same loads (past the last step they repeat it into a free slot), which keeps that count
+// exact. One wave per SIMD issues every instruction of its step itself, so the step keeps them few:
+// the load addresses advance by scalar increments, the causal mask costs nothing off the diagonal
+// (on a diagonal step a masked pair gets lse = +inf, hence P = 0 and dS = 0), and P and dS go to
+// bf16 as they are formed.
+constexpr int DKDV_NBUF = 4;
+struct DkdvRows {    // Q, dO rows: chunk x of row r in slot x ^ (r & 15) (unpadded, conflict-free reads)
+  uint16_t q[32 * 128], g[32 * 128];
+};
+struct DkdvTrans {   // Q^T, dO^T rows in slot order: chunk x of row d in slot x ^ ((d >> 2) & 3)
+  uint16_t qt[128 * 32], gt[128 * 32];
+};
+struct DkdvStats {   // lse * log2(e) and Delta of the step's 32 queries
+  float l[32], d[32];
+};
+constexpr int DKDV_LOADS_PER_ITER = 9;  // per thread: 4 row chunks, 4 transposed chunks, 1 stats word
+
+// Scalar position of the load streams in the step sequence. Step j is query head hk G + j / per_head,
+// 32-query block nqb - 1 - j % per_head; x = (b Hq + head) S + q0 and t = (b Hq + head) 128 S + q0 are
+// the element offsets of its Q/dO rows (x 128), its transposed columns (t) and its lse/Delta (x).
+struct DkdvStream {
+  int64_t x, t;
+  int left;   // steps of the current head from j on
+  int j;
+};
+__device__ __forceinline__ void dkdv_advance(DkdvStream& s, int nsteps, int per_head, int S) {
+  if (s.j + 1 >= nsteps) return;  // past the last step the loads repeat it
+  ++s.j;
+  const bool wrap = --s.left == 0;
+  s.left = wrap ? per_head : s.left;
+  s.x += wrap ? (int64_t)S + 32 * (per_head - 1) : -32;
+  s.t += wrap ? (int64_t)128 * S + 32 * (per_head - 1) : -32;
+}
+// Per-lane byte offsets of a thread's chunks: thread tid fills LDS chunks 256 i + tid (i = 0, 1; 16
+// bytes each; each wave's 64 chunks of one instruction are contiguous) of each tile: of Q and dO, row
+// r = c/16, slot c%16, holding chunk (c%16) ^ (r & 15) of that query's row; of Q^T and dO^T, row
+// d = c/4, slot c%4, holding chunk (c%4) ^ ((d >> 2) & 3) of the block's 64 bytes of row d (S <= 2^24
+// keeps 2 (127 S + 24) below 2^32). The lse and Delta words come in a quarter per wave (lanes
+// 16w .. 16w + 15 of wave w), so that every thread issues the same number of loads.
+struct DkdvLanes {
+  uint32_t roff[2], toff[2], soff;
+  bool sl;  // this lane loads a stats word
+};
+// One iteration's loads (rows of one step, transposed tiles of another, stats of a third), issued in
+// nine parts so that they can be spread over the iteration: part k < 8 is one 16-byte chunk per thread
+// of a tile, part 8 the stats word.
+struct DkdvLoads {
+  const uint16_t *qr, *gr, *qt, *gt;
+  const void* sb;
+  DkdvRows* __restrict__ R;
+  DkdvTrans* __restrict__ T;
+  DkdvStats* __restrict__ St;
+  __device__ __forceinline__ DkdvLoads(const BwdParams& P, int64_t xr, int64_t tt, int64_t xs, DkdvRows* R_,
+                                       DkdvTrans* T_, DkdvStats* St_, int wave_u)
+      : qr(P.qd + xr * 128), gr(P.gd + xr * 128), qt(P.qdt + tt), gt(P.gdt + tt),
+        sb(wave_u < 2 ? (const void*)(P.lse2 + xs) : (const void*)(P.delta + xs - 32)), R(R_), T(T_), St(St_) {}
+  __device__ __forceinline__ void part(int k, const DkdvLanes& L, int wave_u) const {
+    const int i = k & 1, lo = 16 * (256 * i + 64 * wave_u);
+    if (k < 2) dma_lds16(qr, L.roff[i], reinterpret_cast<uint8_t*>(R->q) + lo);
+    else if (k < 4) dma_lds16(gr, L.roff[i], reinterpret_cast<uint8_t*>(R->g) + lo);
+    else if (k < 6) dma_lds16(qt, L.toff[i], reinterpret_cast<uint8_t*>(T->qt) + lo);
+    else if (k < 8) dma_lds16(gt, L.toff[i], reinterpret_cast<uint8_t*>(T->gt) + lo);
+    else if (L.sl) dma_lds4(sb, L.soff, St->l);
   }
-  // operands of group k: rows 16(k/4) + n of Q and dO (step k%4 over D), row 16k + n of the transposes
-  auto rowoff = [&](int k) { return (16 * (k >> 2) + n) * 128 + 8 * ((4 * (k & 3) + g) ^ n); };
-  const int troff = n * 32 + 8 * (g ^ ((n >> 2) & 3));
-  v8bf qa = ld8bf(Tn->q + rowoff(0)), ga = ld8bf(Tn->g + rowoff(0));
-  v8bf gta = ld8bf(Tp->gt + troff), qta = ld8bf(Tp->qt + troff);
+  __device__ __forceinline__ void all(const DkdvLanes& L, int wave_u) const {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) part(k, L, wave_u);
+  }
+};
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {  // round to nearest even
+  const v2bf r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// One iteration of the pipelined dK/dV loop (see above). The LDS slots are restrict pointers. Past the
+// last step Rn is a stale slot (its products are unused). P and dS of step st (bf16 pairs of
+// accumulator elements 2k, 2k + 1) replace those of step st - 1 (pw, sw) at the end.
+__device__ __forceinline__ void dkdv_pipe_iter(const DkdvLoads& ld, const DkdvLanes& Ln, int wave_u,
+                                               const DkdvRows* __restrict__ Rn, const DkdvTrans* __restrict__ Tp,
+                                               const DkdvStats* __restrict__ Sc, int koff, int n, int g,
+                                               float scale_log2, const v8bf (&kop)[8], const v8bf (&vop)[8],
+                                               v16f (&dkT)[4], v16f (&dvT)[4], const v16f& sc, const v16f& pc,
+                                               v16f& sn, v16f& pn, uint32_t (&pw)[8], uint32_t (&sw)[8]) {
+  ld.part(8, Ln, wave_u);
+  float lv[16], dv[16];  // element i: query 8(i/4) + 4g + i%4
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 l4 = *reinterpret_cast<const float4*>(Sc->l + 8 * j + 4 * g);
+    const float4 d4 = *reinterpret_cast<const float4*>(Sc->d + 8 * j + 4 * g);
+    lv[4 * j] = l4.x; lv[4 * j + 1] = l4.y; lv[4 * j + 2] = l4.z; lv[4 * j + 3] = l4.w;
+    dv[4 * j] = d4.x; dv[4 * j + 1] = d4.y; dv[4 * j + 2] = d4.z; dv[4 * j + 3] = d4.w;
+  }
+  if (koff > -31) {  // a key of this wave may lie after a query of the block: mask through lse
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (n + koff > 8 * (i >> 2) + 4 * g + (i & 3)) lv[i] = INFINITY;
+  }
+  // Operands of group k: row n of Q and dO, columns 16k + 8g (chunk 2k + g); row 32(k/2) + n of the
+  // transposes, slots 16(k%2) + 8g (chunk 2(k%2) + g).
+  auto rowoff = [&](int k) { return n * 128 + 8 * ((2 * k + g) ^ (n & 15)); };
+  auto troff = [&](int k) { return (32 * (k >> 1) + n) * 32 + 8 * ((2 * (k & 1) + g) ^ ((n >> 2) & 3)); };
+  v8bf qa = ld8bf(Rn->q + rowoff(0)), ga = ld8bf(Rn->g + rowoff(0));
+  v8bf gta = ld8bf(Tp->gt + troff(0)), qta = ld8bf(Tp->qt + troff(0));
+  uint32_t npw[8], nsw[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     v8bf qa2, ga2, gta2, qta2;
     if (k < 7) {  // the next group's operands, read one group ahead
-      qa2 = ld8bf(Tn->q + rowoff(k + 1));
-      ga2 = ld8bf(Tn->g + rowoff(k + 1));
-      gta2 = ld8bf(Tp->gt + 16 * 32 * (k + 1) + troff);
-      qta2 = ld8bf(Tp->qt + 16 * 32 * (k + 1) + troff);
+      qa2 = ld8bf(Rn->q + rowoff(k + 1));
+      ga2 = ld8bf(Rn->g + rowoff(k + 1));
+      gta2 = ld8bf(Tp->gt + troff(k + 1));
+      qta2 = ld8bf(Tp->qt + troff(k + 1));
     }
-    const int mt = k >> 2, s4 = k & 3;
-    sn[mt] = mfma16(qa, kop[s4], sn[mt]);
-    pn[mt] = mfma16(ga, vop[s4], pn[mt]);
-    dvT[k] = mfma16(gta, pbp, dvT[k]);
-    dkT[k] = mfma16(qta, sbp, dkT[k]);
-    {  // P and dS of element (mt, i) = (k/4, k%4) of step st; query 16mt + 4g + i, key key0 + n
-      const int i = k & 3;
-      float p = __builtin_amdgcn_exp2f(fmaf(sc[mt][i], scale_log2, -lv[k]));
-      if (n + koff > 16 * mt + 4 * g + i) p = 0.f;  // key after query
-      sc[mt][i] = p;
-      pc[mt][i] = p * (pc[mt][i] - dv[k]);
+    ld.part(k, Ln, wave_u);
+    sn = k == 0 ? mfma_bf16(qa, kop[0], v16f{}) : mfma_bf16(qa, kop[k], sn);
+    pn = k == 0 ? mfma_bf16(ga, vop[0], v16f{}) : mfma_bf16(ga, vop[k], pn);
+    {
+      const int t = k & 1;
+      const v8bf pb = __builtin_bit_cast(v8bf, uint4{pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]});
+      const v8bf sb = __builtin_bit_cast(v8bf, uint4{sw[4 * t], sw[4 * t + 1], sw[4 * t + 2], sw[4 * t + 3]});
+      dvT[k >> 1] = mfma_bf16(gta, pb, dvT[k >> 1]);
+      dkT[k >> 1] = mfma_bf16(qta, sb, dkT[k >> 1]);
+    }
+    {  // P and dS of elements 2k, 2k + 1 of step st (query 8(i/4) + 4g + i%4, key key0 + n)
+      const int i = 2 * k;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], scale_log2, -lv[i]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], scale_log2, -lv[i + 1]));
+      npw[k] = pack_bf16(p0, p1);
+      nsw[k] = pack_bf16(p0 * (pc[i] - dv[i]), p1 * (pc[i + 1] - dv[i + 1]));
     }
     if (k < 7) {
       qa = qa2; ga = ga2; gta = gta2; qta = qta2;
     }
+    // Issue order of the group: the next group's four operand reads, then the four MFMAs with the
+    // VALU work between them (the compiler would otherwise read each operand just before its MFMA).
+    if (k == 0) __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+    if (k < 7) __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0002, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0002, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0002, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0002, 2, 0);
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {  // slot (g, e) of the next dV/dK products: query 16(e/4) + 4g + e%4
-    pbp[e] = (__bf16)sc[e >> 2][e & 3];
-    sbp[e] = (__bf16)pc[e >> 2][e & 3];
+  for (int e = 0; e < 8; ++e) {
+    pw[e] = npw[e];
+    sw[e] = nsw[e];
   }
-  // The loads issued at the top of this iteration (step st + 2) complete here; the barrier publishes them.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Iteration st + 1 reads the loads issued in iteration st - 2 (or before the loop): wait until at
+  // most the last two iterations' loads are in flight; the barrier publishes them.
+  static_assert(2 * DKDV_LOADS_PER_ITER <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * DKDV_LOADS_PER_ITER & 15) | ((2 * DKDV_LOADS_PER_ITER >> 4) << 14));
   __syncthreads();
 }
 
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(const BwdParams P) {
-  __shared__ __align__(16) DkdvTiles buf[DKDV_NBUF];
-  const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams P) {
+  __shared__ __align__(16) DkdvRows rows[DKDV_NBUF];
+  __shared__ __align__(16) DkdvTrans trans[DKDV_NBUF];
+  __shared__ __align__(16) DkdvStats stats[DKDV_NBUF];
+  const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, g = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int kt = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // Longest first: id / (Hkv B) is the key tile (tile kt has the most query blocks at kt = 0).
+  const int nbh = P.Hkv * P.B, id = (int)blockIdx.x;
+  const int kt = id / nbh, bh = id - kt * nbh, b = bh / P.Hkv, hk = bh - b * P.Hkv;
   const int G = P.Hq / P.Hkv;
-  const int key0 = 128 * kt + 16 * wave;
-  const bool valid = key0 < S;  // S % 32 == 0: a wave's 16 keys are all inside or all outside
+  const int key0 = 128 * kt + 32 * wave, key0_u = 128 * kt + 32 * wave_u;
+  const bool valid = key0 < S;  // S % 32 == 0: a wave's 32 keys are all inside or all outside
   const int64_t bhk = (int64_t)b * P.Hkv + hk;
-  // B operands: lane (key n, g), step s holds columns 32s + 8g + [0, 8) of the key's K and V rows.
-  v8bf kop[4], vop[4];
+  // B operands: lane (key n, g), step s holds columns 16s + 8g + [0, 8) of the key's K and V rows.
+  v8bf kop[8], vop[8];
   const int krow = valid ? key0 + n : 0;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    kop[s] = ld8bf(P.kd + (bhk * S + krow) * 128 + 32 * s + 8 * g);
-    vop[s] = ld8bf(P.vd + (bhk * S + krow) * 128 + 32 * s + 8 * g);
+  for (int s = 0; s < 8; ++s) {
+    kop[s] = ld8bf(P.kd + (bhk * S + krow) * 128 + 16 * s + 8 * g);
+    vop[s] = ld8bf(P.vd + (bhk * S + krow) * 128 + 16 * s + 8 * g);
   }
-  v4f dkT[8], dvT[8];  // tile dt: lane (key n, g), element i <-> column d = 16dt + 4g + i
+  v16f dkT[4], dvT[4];  // tile dt: lane (key n, g), element i <-> column d = 32dt + 8(i/4) + 4g + i%4
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) dkT[dt][i] = dvT[dt][i] = 0.f;
   const int nqb = S / 32, qb0 = 4 * kt, per_head = nqb - qb0, nsteps = G * per_head;
-  // this thread's LDS chunk of the tiles (row and source chunk; the fetch below)
-  const int rr = tid >> 4, rx = (tid & 15) ^ (rr & 15), td = tid >> 2, tx = (tid & 3) ^ ((td >> 2) & 3);
-  // Slot 3 stands in for step -1 in iteration 0: zero transposed tiles, which with zero P and dS add
+  DkdvLanes L;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = 256 * i + tid, r = c >> 4, x = (c & 15) ^ (r & 15), d = c >> 2, xt = (c & 3) ^ ((d >> 2) & 3);
+    L.roff[i] = 2u * (uint32_t)(r * 128 + 8 * x);
+    L.toff[i] = 2u * ((uint32_t)d * (uint32_t)S + 8u * (uint32_t)xt);
+  }
+  L.soff = 4u * (uint32_t)lane;  // words 0..31 lse, 32..63 Delta (the Delta base is 32 words lower)
+  L.sl = (lane >> 4) == wave;
+  // Load streams: rows of step i + 4, transposed of step i + 2, stats of step i + 3 in iteration i.
+  DkdvStream st;
+  st.j = 0;
+  st.left = per_head;
+  st.x = ((int64_t)b * P.Hq + hk * G) * S + 32 * (nqb - 1);
+  st.t = ((int64_t)b * P.Hq + hk * G) * 128 * S + 32 * (nqb - 1);
+  // Transposed slot 3 stands in for step -1 in iteration 0: zero tiles, which with zero P and dS add
   // exactly 0. Step 3 first arrives there in iteration 1.
   {
-    uint4* z0 = reinterpret_cast<uint4*>(buf[DKDV_NBUF - 1].qt);
-    uint4* z1 = reinterpret_cast<uint4*>(buf[DKDV_NBUF - 1].gt);
-    z0[tid] = uint4{0u, 0u, 0u, 0u};
-    z1[tid] = uint4{0u, 0u, 0u, 0u};
+    uint4* z0 = reinterpret_cast<uint4*>(trans[DKDV_NBUF - 1].qt);
+    uint4* z1 = reinterpret_cast<uint4*>(trans[DKDV_NBUF - 1].gt);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) z0[256 * i + tid] = z1[256 * i + tid] = uint4{0u, 0u, 0u, 0u};
   }
-  dkdv_fetch(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[0], 0, b, hk, G, per_head, nqb, S, P.Hq, rr, rx, td, tx,
-             lane, wave_u);
-  if (nsteps > 1)
-    dkdv_fetch(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[1], 1, b, hk, G, per_head, nqb, S, P.Hq, rr, rx, td, tx,
-               lane, wave_u);
+  // Before the loop: rows of steps 0..3, transposed of steps 0, 1, stats of steps 0..2 (the stream
+  // positions of steps 0..4 pass by; the loop starts with rows at 4, stats at 3, transposed at 2).
+  int64_t x3, t2, t3;
+  {
+    int64_t xs[4], ts[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xs[j] = st.x; ts[j] = st.t;
+      dkdv_advance(st, nsteps, per_head, S);
+    }
+    // steps 2 and 3 bring transposed tiles the loop loads again (into slot 2, reloaded in iteration 0;
+    // slot 3 keeps its zeros) and step 3 stats the loop loads again
+    DkdvLoads(P, xs[0], ts[0], xs[0], &rows[0], &trans[0], &stats[0], wave_u).all(L, wave_u);
+    DkdvLoads(P, xs[1], ts[1], xs[1], &rows[1], &trans[1], &stats[1], wave_u).all(L, wave_u);
+    DkdvLoads(P, xs[2], ts[2], xs[2], &rows[2], &trans[2], &stats[2], wave_u).all(L, wave_u);
+    DkdvLoads(P, xs[3], ts[3], xs[3], &rows[3], &trans[2], &stats[3], wave_u).all(L, wave_u);
+    x3 = xs[3]; t2 = ts[2]; t3 = ts[3];
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   // S and dP of step 0
-  v4f sa[2], pa[2], sb[2], pb2[2];
+  v16f sa, pa, sb2, pb2;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int i = 0; i < 16; ++i) sa[i] = pa[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[mt][i] = pa[mt][i] = 0.f;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int off = (16 * mt + n) * 128 + 8 * ((4 * s4 + g) ^ n);
-      sa[mt] = mfma16(ld8bf(buf[0].q + off), kop[s4], sa[mt]);
-      pa[mt] = mfma16(ld8bf(buf[0].g + off), vop[s4], pa[mt]);
-    }
+  for (int s = 0; s < 8; ++s) {
+    const int off = n * 128 + 8 * ((2 * s + g) ^ (n & 15));
+    sa = mfma_bf16(ld8bf(rows[0].q + off), kop[s], sa);
+    pa = mfma_bf16(ld8bf(rows[0].g + off), vop[s], pa);
   }
-  v8bf pbp, sbp;  // P and dS of the previous step (none before step 0)
+  uint32_t pw[8], sw[8];  // P and dS of the previous step as bf16 pairs (none before step 0)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pbp[e] = sbp[e] = (__bf16)0.f;
-  // unrolled by four: ring slots are constants (step st in slot st % 4); S and dP buffers alternate
-  auto it4 = [&](auto kslot, int st, v4f (&sc)[2], v4f (&pc)[2], v4f (&sn)[2], v4f (&pn)[2]) {
+  for (int e = 0; e < 8; ++e) pw[e] = sw[e] = 0u;
+  // unrolled by four: ring slots are constants (step i in slot i % 4); S and dP buffers alternate
+  auto it4 = [&](auto kslot, int i, v16f& sc, v16f& pc, v16f& sn, v16f& pn) {
     constexpr int s = decltype(kslot)::value;
-    dkdv_pipe_iter(P.qd, P.gd, P.qdt, P.gdt, P.lse2, P.delta, &buf[s], &buf[(s + 1) % DKDV_NBUF],
-                   &buf[(s + 3) % DKDV_NBUF], &buf[(s + 2) % DKDV_NBUF], st, nsteps, b, hk, G, per_head, nqb, S, P.Hq,
-                   rr, rx, td, tx, lane, wave_u, n, g, key0, P.scale_log2, kop, vop, dkT, dvT, sc, pc, sn, pn, pbp,
-                   sbp);
+    const DkdvLoads ld(P, st.x, t2, x3, &rows[s], &trans[(s + 2) % DKDV_NBUF], &stats[(s + 3) % DKDV_NBUF], wave_u);
+    t2 = t3; t3 = st.t; x3 = st.x;
+    dkdv_advance(st, nsteps, per_head, S);
+    const int qb = nqb - 1 - i % per_head;
+    dkdv_pipe_iter(ld, L, wave_u, &rows[(s + 1) % DKDV_NBUF], &trans[(s + 3) % DKDV_NBUF], &stats[s], key0_u - 32 * qb, n, g,
+                   P.scale_log2, kop, vop, dkT, dvT, sc, pc, sn, pn, pw, sw);
   };
-  for (int st = 0; st < nsteps; st += 4) {
-    it4(std::integral_constant<int, 0>{}, st, sa, pa, sb, pb2);
-    if (st + 1 < nsteps) it4(std::integral_constant<int, 1>{}, st + 1, sb, pb2, sa, pa);
-    if (st + 2 < nsteps) it4(std::integral_constant<int, 2>{}, st + 2, sa, pa, sb, pb2);
-    if (st + 3 < nsteps) it4(std::integral_constant<int, 3>{}, st + 3, sb, pb2, sa, pa);
+  for (int i = 0; i < nsteps; i += 4) {
+    it4(std::integral_constant<int, 0>{}, i, sa, pa, sb2, pb2);
+    if (i + 1 < nsteps) it4(std::integral_constant<int, 1>{}, i + 1, sb2, pb2, sa, pa);
+    if (i + 2 < nsteps) it4(std::integral_constant<int, 2>{}, i + 2, sa, pa, sb2, pb2);
+    if (i + 3 < nsteps) it4(std::integral_constant<int, 3>{}, i + 3, sb2, pb2, sa, pa);
   }
+  // Every load has landed (also the repeats past the last step, which must not outlive the workgroup).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   {  // dV and dK of the last step
-    const DkdvTiles& Tp = buf[(nsteps - 1) % DKDV_NBUF];
-    const int troff = n * 32 + 8 * (g ^ ((n >> 2) & 3));
+    const DkdvTrans& Tp = trans[(nsteps - 1) % DKDV_NBUF];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      dvT[k] = mfma16(ld8bf(Tp.gt + 16 * 32 * k + troff), pbp, dvT[k]);
-      dkT[k] = mfma16(ld8bf(Tp.qt + 16 * 32 * k + troff), sbp, dkT[k]);
+      const int off = (32 * (k >> 1) + n) * 32 + 8 * ((2 * (k & 1) + g) ^ ((n >> 2) & 3));
+      const int t = k & 1;
+      const v8bf pb = __builtin_bit_cast(v8bf, uint4{pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]});
+      const v8bf sb = __builtin_bit_cast(v8bf, uint4{sw[4 * t], sw[4 * t + 1], sw[4 * t + 2], sw[4 * t + 3]});
+      dvT[k >> 1] = mfma_bf16(ld8bf(Tp.gt + off), pb, dvT[k >> 1]);
+      dkT[k >> 1] = mfma_bf16(ld8bf(Tp.qt + off), sb, dkT[k >> 1]);
     }
   }
   if (!valid) return;
-  // lane (key n, g), element i of tile dt: column 16dt + 4g + i
+  // lane (key n, g), element i of tile dt: column 32dt + 8(i/4) + 4g + i%4
   const int64_t off = b * P.ksb + (int64_t)(key0 + n) * P.kss + hk * P.ksh + 4 * g;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    uint2 pk, pv;
-    pk.x = f32_to_bf16(dkT[dt][0] * P.scale) | (f32_to_bf16(dkT[dt][1] * P.scale) << 16);
-    pk.y = f32_to_bf16(dkT[dt][2] * P.scale) | (f32_to_bf16(dkT[dt][3] * P.scale) << 16);
-    pv.x = f32_to_bf16(dvT[dt][0]) | (f32_to_bf16(dvT[dt][1]) << 16);
-    pv.y = f32_to_bf16(dvT[dt][2]) | (f32_to_bf16(dvT[dt][3]) << 16);
-    *reinterpret_cast<uint2*>(P.dk + off + 16 * dt) = pk;
-    *reinterpret_cast<uint2*>(P.dv + off + 16 * dt) = pv;
-  }
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint2 pk, pv;
+      pk.x = f32_to_bf16(dkT[dt][4 * j] * P.scale) | (f32_to_bf16(dkT[dt][4 * j + 1] * P.scale) << 16);
+      pk.y = f32_to_bf16(dkT[dt][4 * j + 2] * P.scale) | (f32_to_bf16(dkT[dt][4 * j + 3] * P.scale) << 16);
+      pv.x = f32_to_bf16(dvT[dt][4 * j]) | (f32_to_bf16(dvT[dt][4 * j + 1]) << 16);
+      pv.y = f32_to_bf16(dvT[dt][4 * j + 2]) | (f32_to_bf16(dvT[dt][4 * j + 3]) << 16);
+      *reinterpret_cast<uint2*>(P.dk + off + 32 * dt + 8 * j) = pk;
+      *reinterpret_cast<uint2*>(P.dv + off + 32 * dt + 8 * j) = pv;
+    }
 }
 
 // ---- dQ ----------------------------------------------------------------------------------------
@@ -394,7 +507,9 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   __shared__ __align__(16) DqTiles buf[2];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int qt = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  // Longest first: the last query tile (the most key blocks) of every (b, hq) comes first.
+  const int nbh = P.Hq * P.B, id = (int)blockIdx.x, ntiles = (S + 127) / 128;
+  const int qt = ntiles - 1 - id / nbh, bh = id - (id / nbh) * nbh, b = bh / P.Hq, hq = bh - b * P.Hq;
   const int hk = hq / (P.Hq / P.Hkv);
   const int qb = 4 * qt + wave, q0 = 32 * qb;
   const bool valid = q0 < S;
@@ -435,37 +550,49 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if (kb + 1 < nkb) fetch(kb + 1, buf[(kb + 1) & 1]);
     __builtin_amdgcn_sched_barrier(0);
     const DqTiles& T = buf[kb & 1];
-    {  // branch-free as in the dK/dV kernel
-      // S^T = K Q^T and dP^T = V dO^T: lane (query c, h), element i <-> key 8(i/4) + 4h + i%4 of the block
-      v8bf ka[8], va[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int off = c * 128 + 8 * ((2 * s + h) ^ (c & 15));  // columns 16s + 8h: chunk 2s + h
-        ka[s] = ld8bf(T.k + off);
-        va[s] = ld8bf(T.v + off);
-      }
+    {
+      // S^T = K Q^T and dP^T = V dO^T: lane (query c, h), element i <-> key 8(i/4) + 4h + i%4 of the
+      // block. The K and V operands of step s + 1 are read while the MFMAs of step s run, and the K^T
+      // operands of the dQ products (row 32dt + c, chunk 2t + h) during the first four steps.
+      auto off = [&](int s) { return c * 128 + 8 * ((2 * s + h) ^ (c & 15)); };  // columns 16s + 8h
+      v8bf ka = ld8bf(T.k + off(0)), va = ld8bf(T.v + off(0));
+      v8bf kta[2][4];
       v16f sacc, pacc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
-#pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sacc = mfma_bf16(ka[s], qop[s], sacc);
-        pacc = mfma_bf16(va[s], gop[s], pacc);
+        v8bf ka2, va2;
+        if (s < 7) {
+          ka2 = ld8bf(T.k + off(s + 1));
+          va2 = ld8bf(T.v + off(s + 1));
+        }
+        if (s < 4) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int t = (2 * s + u) >> 2, dt = (2 * s + u) & 3;
+            kta[t][dt] = ld8bf(T.kt + (32 * dt + c) * 32 + 8 * ((2 * t + h) ^ ((c >> 2) & 3)));
+          }
+        }
+        sacc = s == 0 ? mfma_bf16(ka, qop[0], v16f{}) : mfma_bf16(ka, qop[s], sacc);
+        pacc = s == 0 ? mfma_bf16(va, gop[0], v16f{}) : mfma_bf16(va, gop[s], pacc);
+        if (s < 7) {
+          ka = ka2;
+          va = va2;
+        }
+        if (s < 4) __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+        else if (s < 7) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);
       }
-      v8bf kta[2][4];
+      float pv[16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lse2));
+      if (kb >= qb) {  // the block reaches this wave's queries: mask key > query
+        const int qoff = 32 * (qb - kb);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)  // row 32dt + c, chunk 2t + h
-          kta[t][dt] = ld8bf(T.kt + (32 * dt + c) * 32 + 8 * ((2 * t + h) ^ ((c >> 2) & 3)));
-      const int qoff = 32 * (qb - kb);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lse2));
-        if (kk > qoff + c) p = 0.f;  // key after query (whole block when kb > qb)
-        pacc[i] = p * (pacc[i] - del);  // dS^T
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + 4 * h + (i & 3) > qoff + c) pv[i] = 0.f;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pacc[i] = pv[i] * (pacc[i] - del);  // dS^T
       // dQ^T += K^T dS^T over the 32 keys, two 16-key steps: B slot (h, e) of step t is accumulator
       // element 8t + e, key 16t + 8(e/4) + 4h + e%4, the order (dq_tpos) of the K^T tile's rows
 #pragma unroll
@@ -502,7 +629,7 @@ hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* 
                                                                           (unsigned)B);
   bwd_prep_kernel<0, 1><<<tq, 256, 0, stream>>>(qc, qs, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hq, ws.qd, ws.qdt,
                                                    nullptr);
-  bwd_prep_kernel<0, 2><<<tk, 256, 0, stream>>>(kc, ks, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.kd, ws.kdt, nullptr);
+  bwd_prep_kernel<0, 1><<<tk, 256, 0, stream>>>(kc, ks, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.kd, ws.kdt, nullptr);
   bwd_prep_kernel<1><<<tk, 256, 0, stream>>>(vt, vta, nullptr, 0, 0, 0, nullptr, 0, 0, 0, S, Hkv, ws.vd, nullptr,
                                              nullptr);
   bwd_prep_kernel<2, 1><<<tq, 256, 0, stream>>>(nullptr, nullptr, dout, qsb, qss, qsh, o, qsb, qss, qsh, S, Hq,
@@ -510,14 +637,14 @@ hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* 
   BwdParams p{};
   p.qd = ws.qd; p.qdt = ws.qdt; p.kd = ws.kd; p.kdt = ws.kdt; p.vd = ws.vd; p.gd = ws.gd; p.gdt = ws.gdt;
   p.lse = lse; p.delta = ws.delta; p.lse2 = ws.lse2;
-  p.S = S; p.Hq = Hq; p.Hkv = Hkv;
+  p.B = B; p.S = S; p.Hq = Hq; p.Hkv = Hkv;
   p.scale = softmax_scale;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.qsb = qsb; p.qss = qss; p.qsh = qsh; p.ksb = ksb; p.kss = kss; p.ksh = ksh;
   const unsigned tiles = (unsigned)((S + 127) / 128);
-  bwd_dkdv_kernel<<<dim3(tiles, (unsigned)Hkv, (unsigned)B), 512, 0, stream>>>(p);
-  bwd_dq_kernel<<<dim3(tiles, (unsigned)Hq, (unsigned)B), 256, 0, stream>>>(p);
+  bwd_dkdv_kernel<<<dim3(tiles * (unsigned)Hkv * (unsigned)B), 256, 0, stream>>>(p);
+  bwd_dq_kernel<<<dim3(tiles * (unsigned)Hq * (unsigned)B), 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
