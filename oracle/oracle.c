@@ -21,8 +21,10 @@
  *   R6  P of the completed blocks is quantised with one E8M0 per (query row,
  *       32-key block aligned to multiples of 32) on p = 2^(t - T), T an integer
  *       upper bound of the row's max of t = scale*log2(e)*q.k; the normaliser l
- *       sums the unquantised p. The code of p is decided on p rounded to fp32,
- *       the precision in which the GPU kernel holds P.
+ *       sums the unquantised p. The code of p is decided on p rounded to fp32:
+ *       the PR's tests check the MXFP8 path against an FP32 attention
+ *       reference [TE#3865 commits], so P exists as an fp32 tensor before it
+ *       is quantised.
  *   R7  Own block: s = scale * q.k on decoded MXFP8 Q/K, p = e^(s - max s) in
  *       full precision (not quantised), V from the token-normalised copy.
  *   R8  A row with no completed key (i < 32) has O_c = 0, lse_c = -inf.
