@@ -13,22 +13,22 @@
 //    for the MFMA operands that contract over tokens; it also forms Delta.
 //  * dK/dV kernel: one wave per 32 keys, one wave per SIMD (its 512 registers hold the K and V
 //    operands, both accumulators and a whole pipelined step). For every query head of the KV head and
-//    every 32-query block at or after the
-//    keys, it computes S = Q K^T and dP = dO V^T (keys on the lanes, queries on the accumulator
-//    elements), P and dS elementwise, and accumulates dV^T += dO^T P and dK^T += Q^T dS. P and dS stay
-//    in their accumulator registers and are the B operand of those MFMAs: the accumulator's query
-//    order is a permutation of the B operand's contraction order, and the A operand (dO^T, Q^T, read
-//    from LDS) is read in the same permuted order. The steps are software-pipelined.
-//  * dQ kernel: one wave per 32 queries, their Q and dO operands in registers. For every 32-key block
-//    at or before the queries it computes S^T = K Q^T and dP^T = V dO^T (queries on the lanes: lse and
-//    Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way.
-//  * Key > query is masked to P = 0. The loops start at the workgroup's first block on or below the
-//    diagonal, so a wave whose own blocks start later computes at most three fully masked steps; that
-//    keeps the loop branch-free per wave.
-//  * Query (dK/dV) and key (dQ) blocks go from global memory straight into an LDS ring shared by the
-//    workgroup (loads with the LDS flag, issued a step or two ahead; no register staging). Rows are
-//    unpadded and the 16-byte chunks XOR-swizzled, so the operand reads are bank-conflict-free; the
-//    preparation pass writes the transposed copies in each kernel's MFMA slot order.
+//    every 32-query block at or after the keys, it computes S = Q K^T and dP = dO V^T (keys on the
+//    lanes, queries on the accumulator elements), P and dS elementwise, and accumulates
+//    dV^T += dO^T P and dK^T += Q^T dS. P and dS are the B operand of those MFMAs straight from the
+//    accumulator layout: the accumulator's query order is a permutation of the B operand's
+//    contraction order, and the A operand (dO^T, Q^T, read from LDS) is stored in the same permuted
+//    order. The steps are software-pipelined.
+//  * dQ kernel: one wave per 32 queries, two waves per SIMD, their Q and dO operands in registers. For
+//    every 32-key block at or before the queries it computes S^T = K Q^T and dP^T = V dO^T (queries on
+//    the lanes: lse and Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way.
+//  * Key > query is masked to P = 0, only on the steps that straddle the diagonal. The loops start at
+//    the workgroup's first block on or below the diagonal, so a wave whose own blocks start later
+//    computes at most three fully masked steps.
+//  * Query (dK/dV) and key (dQ) blocks go from global memory straight into LDS rings shared by the
+//    workgroup (loads with the LDS flag; no register staging). Rows are unpadded and the 16-byte
+//    chunks XOR-swizzled, so the operand reads are bank-conflict-free; the preparation pass writes the
+//    transposed copies in the MFMA slot order. Both grids run the longest workgroups first.
 #include "device_common.h"
 #include "launch.h"
 
