@@ -64,11 +64,18 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(const uint16_t* __restr
   const int s0 = blockIdx.x * VQ_TOK, h = blockIdx.y, b = blockIdx.z;
   const int ntok = min(VQ_TOK, S - s0);  // a multiple of 32
   const int64_t bh = (int64_t)b * H + h;
-  for (int c = tid; c < ntok * 16; c += 256) {
-    const int r = c >> 4, q = c & 15;
-    const uint4 val = *reinterpret_cast<const uint4*>(v + b * sb + (int64_t)(s0 + r) * ss + h * sh + q * 8);
-    *reinterpret_cast<uint4*>(tile + r * VQ_ROW + q * 8) = val;
+  // Thread tid moves chunk tid % 16 of rows tid / 16 + 16 i: all its loads are issued before any is
+  // waited for (rows past the last token re-read the last one; only rows < ntok are read back).
+  constexpr int kLoads = VQ_TOK / 16;
+  const int q = tid & 15;
+  uint4 val[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = min((tid >> 4) + 16 * i, ntok - 1);
+    val[i] = *reinterpret_cast<const uint4*>(v + b * sb + (int64_t)(s0 + r) * ss + h * sh + q * 8);
   }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) *reinterpret_cast<uint4*>(tile + ((tid >> 4) + 16 * i) * VQ_ROW + q * 8) = val[i];
   __syncthreads();
 
   // Token-normalised copy: two threads per token, 64 elements each.
