@@ -143,7 +143,11 @@ __device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t r, void* lds,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
+// kFresh: the slot addresses are formed here from an opaque copy of tid (the ordinary causal variant,
+// which has no register to keep them in across its loop).
+template <bool kFresh>
 __device__ __forceinline__ void store_scales(TileSmem& t, uint32_t sc, int tid) {
+  if (kFresh) asm volatile("" : "+v"(tid));
   if (tid < 64) {
     // bytes s0 s2 s1 s3: the 16-bit half hf then holds the scales of D-blocks hf and 2 + hf
     t.ks[k_lds_row(tid)] = __builtin_amdgcn_perm(sc, sc, 0x03010200u);
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
   if (ntiles > 0) {
     TILE_LOAD(sm[0], psc, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    store_scales(sm[0], psc, tid);
+    store_scales<kLeaky>(sm[0], psc, tid);
   }
   __syncthreads();
   // One 64-key tile per iteration, double-buffered. The score MFMAs of tile it come first; then the
@@ -496,7 +500,7 @@ __global__ __launch_bounds__(256, 3) void attn_kernel(const AttnParams P) {
     // The next tile's loads (LDS and scale word) are complete here on every path; then its scales
     // are stored and the barrier publishes the tile.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (it + 1 < ntiles) store_scales(sm[s ^ 1], psc, tid);
+    if (it + 1 < ntiles) store_scales<kLeaky>(sm[s ^ 1], psc, tid);
     __syncthreads();
   };
   for (int it = 0; it < ntiles; it += 2) {
