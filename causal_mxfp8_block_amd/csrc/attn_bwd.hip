@@ -21,7 +21,9 @@
 //    order. The steps are software-pipelined.
 //  * dQ kernel: one wave per 32 queries, two waves per SIMD, their Q and dO operands in registers. For
 //    every 32-key block at or before the queries it computes S^T = K Q^T and dP^T = V dO^T (queries on
-//    the lanes: lse and Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way.
+//    the lanes: lse and Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way,
+//    pipelined by one block: the dQ products of a block are issued behind the S and dP products of the
+//    next one, and that block's P and dS are formed while they run.
 //  * Key > query is masked to P = 0, only on the steps that straddle the diagonal. The loops start at
 //    the workgroup's first block on or below the diagonal, so a wave whose own blocks start later
 //    computes at most three fully masked steps.
@@ -497,14 +499,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
 // ---- dQ ----------------------------------------------------------------------------------------
 // Workgroup: 4 waves = queries 128 qt .. 128 qt + 127 of (b, hq); wave w owns queries 32(4qt + w) + [0, 32).
-// Key blocks go from global memory straight into two LDS slots (loads with the LDS flag), one step
-// ahead, as in the dK/dV kernel.
+// Key blocks go from global memory straight into a ring of three LDS slots (loads with the LDS flag),
+// one block ahead. The loop is software-pipelined by one stage: iteration kb issues the S^T and dP^T
+// products of block kb, then the dQ^T products of block kb - 1 (from that block's K^T tile, still in
+// its slot, and its dS kept as bf16 pairs), and forms P and dS of block kb on the VALU while those run;
+// so a wave's VALU work no longer waits behind its own dQ products.
 struct DqTiles {
   uint16_t k[32 * 128], v[32 * 128];  // K, V rows: chunk c of row r in slot c ^ (r & 15)
   uint16_t kt[128 * 32];              // K^T rows (dQ slot order): chunk c of row d in slot c ^ ((d >> 2) & 3)
 };
+constexpr int DQ_NBUF = 3;
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams P) {
-  __shared__ __align__(16) DqTiles buf[2];
+  __shared__ __align__(16) DqTiles buf[DQ_NBUF];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Longest first: the last query tile (the most key blocks) of every (b, hq) comes first.
@@ -542,70 +548,96 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       gload_lds16(kdt + (int64_t)d * S + 32 * kb + 8 * xt, reinterpret_cast<uint8_t*>(T.kt) + lo);
     }
   };
+  // The K^T tile of "block -1" (the slot iteration 0 takes its dQ operands from) is zero: with zero dS
+  // its products add exactly 0.
+  {
+    uint4* z = reinterpret_cast<uint4*>(buf[DQ_NBUF - 1].kt);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) z[256 * i + tid] = uint4{0u, 0u, 0u, 0u};
+  }
   fetch(0, buf[0]);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    // the next key block into the other slot, read last in step kb - 1 (before the barrier ending it)
-    if (kb + 1 < nkb) fetch(kb + 1, buf[(kb + 1) & 1]);
+  uint32_t dsw[8] = {};  // dS^T of the previous block as bf16 pairs: slice t in dsw[4t .. 4t + 3]
+  // dQ^T += K^T dS^T over a block's 32 keys, two 16-key steps: B slot (h, e) of step t is accumulator
+  // element 8t + e, key 16t + 8(e/4) + 4h + e%4, the order (dq_tpos) of the K^T tile's rows
+  auto kt_off = [&](int t, int dt) { return (32 * dt + c) * 32 + 8 * ((2 * t + h) ^ ((c >> 2) & 3)); };
+  auto step = [&](auto kslot, int kb) {
+    constexpr int s0 = decltype(kslot)::value;  // kb % 3
+    // the next key block into the slot of block kb - 2, read last in iteration kb - 1
+    if (kb + 1 < nkb) fetch(kb + 1, buf[(s0 + 1) % DQ_NBUF]);
     __builtin_amdgcn_sched_barrier(0);
-    const DqTiles& T = buf[kb & 1];
-    {
-      // S^T = K Q^T and dP^T = V dO^T: lane (query c, h), element i <-> key 8(i/4) + 4h + i%4 of the
-      // block. The K and V operands of step s + 1 are read while the MFMAs of step s run, and the K^T
-      // operands of the dQ products (row 32dt + c, chunk 2t + h) during the first four steps.
-      auto off = [&](int s) { return c * 128 + 8 * ((2 * s + h) ^ (c & 15)); };  // columns 16s + 8h
-      v8bf ka = ld8bf(T.k + off(0)), va = ld8bf(T.v + off(0));
-      v8bf kta[2][4];
-      v16f sacc, pacc;
+    const DqTiles& T = buf[s0];
+    const DqTiles& Tp = buf[(s0 + DQ_NBUF - 1) % DQ_NBUF];  // block kb - 1
+    // S^T = K Q^T and dP^T = V dO^T: lane (query c, h), element i <-> key 8(i/4) + 4h + i%4 of the
+    // block. The K and V operands of step s + 1 are read while the MFMAs of step s run, and the K^T
+    // operands of block kb - 1 during the first four steps.
+    auto off = [&](int s) { return c * 128 + 8 * ((2 * s + h) ^ (c & 15)); };  // columns 16s + 8h
+    v8bf ka = ld8bf(T.k + off(0)), va = ld8bf(T.v + off(0));
+    v8bf kta[2][4];
+    v16f sacc, pacc;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        v8bf ka2, va2;
-        if (s < 7) {
-          ka2 = ld8bf(T.k + off(s + 1));
-          va2 = ld8bf(T.v + off(s + 1));
-        }
-        if (s < 4) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int t = (2 * s + u) >> 2, dt = (2 * s + u) & 3;
-            kta[t][dt] = ld8bf(T.kt + (32 * dt + c) * 32 + 8 * ((2 * t + h) ^ ((c >> 2) & 3)));
-          }
-        }
-        sacc = s == 0 ? mfma_bf16(ka, qop[0], v16f{}) : mfma_bf16(ka, qop[s], sacc);
-        pacc = s == 0 ? mfma_bf16(va, gop[0], v16f{}) : mfma_bf16(va, gop[s], pacc);
-        if (s < 7) {
-          ka = ka2;
-          va = va2;
-        }
-        if (s < 4) __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
-        else if (s < 7) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);
+    for (int s = 0; s < 8; ++s) {
+      v8bf ka2, va2;
+      if (s < 7) {
+        ka2 = ld8bf(T.k + off(s + 1));
+        va2 = ld8bf(T.v + off(s + 1));
       }
-      float pv[16];
+      if (s < 4) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lse2));
-      if (kb >= qb) {  // the block reaches this wave's queries: mask key > query
-        const int qoff = 32 * (qb - kb);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (8 * (i >> 2) + 4 * h + (i & 3) > qoff + c) pv[i] = 0.f;
+        for (int u = 0; u < 2; ++u) {
+          const int t = (2 * s + u) >> 2, dt = (2 * s + u) & 3;
+          kta[t][dt] = ld8bf(Tp.kt + kt_off(t, dt));
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pacc[i] = pv[i] * (pacc[i] - del);  // dS^T
-      // dQ^T += K^T dS^T over the 32 keys, two 16-key steps: B slot (h, e) of step t is accumulator
-      // element 8t + e, key 16t + 8(e/4) + 4h + e%4, the order (dq_tpos) of the K^T tile's rows
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const v8bf sb = to_bf16(pacc, t);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dqT[dt] = mfma_bf16(kta[t][dt], sb, dqT[dt]);
+      sacc = s == 0 ? mfma_bf16(ka, qop[0], v16f{}) : mfma_bf16(ka, qop[s], sacc);
+      pacc = s == 0 ? mfma_bf16(va, gop[0], v16f{}) : mfma_bf16(va, gop[s], pacc);
+      if (s < 7) {
+        ka = ka2;
+        va = va2;
       }
+      if (s < 4) __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+      else if (s < 7) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);
     }
+    // dQ^T products of block kb - 1, then P and dS of block kb on the VALU while they run
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const v8bf sb = __builtin_bit_cast(v8bf, uint4{dsw[4 * t], dsw[4 * t + 1], dsw[4 * t + 2], dsw[4 * t + 3]});
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) dqT[dt] = mfma_bf16(kta[t][dt], sb, dqT[dt]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x0008, 8, 0);
+    float pv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], P.scale_log2, -lse2));
+    if (kb >= qb) {  // the block reaches this wave's queries: mask key > query
+      const int qoff = 32 * (qb - kb);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + 4 * h + (i & 3) > qoff + c) pv[i] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)  // dS^T as bf16 pairs (elements 2e, 2e + 1)
+      dsw[e] = pack_bf16(pv[2 * e] * (pacc[2 * e] - del), pv[2 * e + 1] * (pacc[2 * e + 1] - del));
     __builtin_amdgcn_sched_barrier(0);
     // The next key block's loads complete here; the barrier publishes them.
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 3) {
+    step(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 < nkb) step(std::integral_constant<int, 1>{}, kb + 1);
+    if (kb + 2 < nkb) step(std::integral_constant<int, 2>{}, kb + 2);
+  }
+  {  // dQ^T products of the last block
+    const DqTiles& Tp = buf[(nkb - 1) % DQ_NBUF];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const v8bf sb = __builtin_bit_cast(v8bf, uint4{dsw[4 * t], dsw[4 * t + 1], dsw[4 * t + 2], dsw[4 * t + 3]});
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) dqT[dt] = mfma_bf16(ld8bf(Tp.kt + kt_off(t, dt)), sb, dqT[dt]);
+    }
   }
   if (!valid) return;
   const int64_t off = b * P.qsb + (int64_t)(q0 + c) * P.qss + hq * P.qsh + 4 * h;
