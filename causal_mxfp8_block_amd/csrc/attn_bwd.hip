@@ -19,14 +19,16 @@
 //    accumulator layout: the accumulator's query order is a permutation of the B operand's
 //    contraction order, and the A operand (dO^T, Q^T, read from LDS) is stored in the same permuted
 //    order. The steps are software-pipelined.
-//  * dQ kernel: one wave per 32 queries, two waves per SIMD, their Q and dO operands in registers. For
+//  * dQ kernel: one wave per 32 queries, their Q and dO operands in registers; 8 waves (256 queries)
+//    per workgroup and one workgroup per CU (two waves per SIMD), so that each K/V tile brought into LDS
+//    serves 256 queries: what the tiles cost is the data moved from L2, not its latency. For
 //    every 32-key block at or before the queries it computes S^T = K Q^T and dP^T = V dO^T (queries on
 //    the lanes: lse and Delta are per-lane scalars) and accumulates dQ^T += K^T dS^T the same way,
 //    pipelined by one block: the dQ products of a block are issued behind the S and dP products of the
 //    next one, and that block's P and dS are formed while they run.
 //  * Key > query is masked to P = 0, only on the steps that straddle the diagonal. The loops start at
 //    the workgroup's first block on or below the diagonal, so a wave whose own blocks start later
-//    computes at most three fully masked steps.
+//    computes at most three (dK/dV) or seven (dQ) fully masked steps.
 //  * Query (dK/dV) and key (dQ) blocks go from global memory straight into LDS rings shared by the
 //    workgroup (loads with the LDS flag; no register staging). Rows are unpadded and the 16-byte
 //    chunks XOR-swizzled, so the operand reads are bank-conflict-free; the preparation pass writes the
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 }
 
 // ---- dQ ----------------------------------------------------------------------------------------
-// Workgroup: 4 waves = queries 128 qt .. 128 qt + 127 of (b, hq); wave w owns queries 32(4qt + w) + [0, 32).
+// Workgroup: 8 waves = queries 256 qt .. 256 qt + 255 of (b, hq); wave w owns queries 32(8qt + w) + [0, 32).
 // Key blocks go from global memory straight into a ring of three LDS slots (loads with the LDS flag),
 // one block ahead. The loop is software-pipelined by one stage: iteration kb issues the S^T and dP^T
 // products of block kb, then the dQ^T products of block kb - 1 (from that block's K^T tile, still in
@@ -509,15 +511,15 @@ struct DqTiles {
   uint16_t kt[128 * 32];              // K^T rows (dQ slot order): chunk c of row d in slot c ^ ((d >> 2) & 3)
 };
 constexpr int DQ_NBUF = 3;
-__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams P) {
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams P) {
   __shared__ __align__(16) DqTiles buf[DQ_NBUF];
   const int S = P.S, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Longest first: the last query tile (the most key blocks) of every (b, hq) comes first.
-  const int nbh = P.Hq * P.B, id = (int)blockIdx.x, ntiles = (S + 127) / 128;
+  const int nbh = P.Hq * P.B, id = (int)blockIdx.x, ntiles = (S + 255) / 256;
   const int qt = ntiles - 1 - id / nbh, bh = id - (id / nbh) * nbh, b = bh / P.Hq, hq = bh - b * P.Hq;
   const int hk = hq / (P.Hq / P.Hkv);
-  const int qb = 4 * qt + wave, q0 = 32 * qb;
+  const int qb = 8 * qt + wave, q0 = 32 * qb;
   const bool valid = q0 < S;
   const int64_t bhq = (int64_t)b * P.Hq + hq, bhk = (int64_t)b * P.Hkv + hk;
   // This wave's Q and dO rows as B operands: lane (query c, h), step s holds columns 16s + 8h + [0, 8).
@@ -535,25 +537,21 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqT[dt][i] = 0.f;
   const uint16_t *kd = P.kd + bhk * S * 128, *vd = P.vd + bhk * S * 128, *kdt = P.kdt + bhk * 128 * S;
-  const int nkb = min(4 * qt + 3, S / 32 - 1) + 1;  // key blocks any wave of the workgroup needs
-  // Thread tid fills LDS chunks ci = tid + 256 i (i = 0, 1; 16 bytes each) of the three tiles: of K and
-  // V, row ci/16, slot ci%16; of K^T, row ci/4, slot ci%4; each wave's 64 chunks are contiguous.
+  const int nkb = min(8 * qt + 7, S / 32 - 1) + 1;  // key blocks any wave of the workgroup needs
+  // Thread tid (of 512) fills LDS chunk ci = tid (16 bytes) of each of the three tiles: of K and V, row
+  // ci/16, slot ci%16; of K^T, row ci/4, slot ci%4; each wave's 64 chunks are contiguous.
   auto fetch = [&](int kb, DqTiles& T) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ci = tid + 256 * i, r = ci >> 4, x = (ci & 15) ^ (r & 15), d = ci >> 2, xt = (ci & 3) ^ ((d >> 2) & 3);
-      const int lo = 16 * (256 * i + 64 * wave_u);
-      gload_lds16(kd + (int64_t)(32 * kb + r) * 128 + 8 * x, reinterpret_cast<uint8_t*>(T.k) + lo);
-      gload_lds16(vd + (int64_t)(32 * kb + r) * 128 + 8 * x, reinterpret_cast<uint8_t*>(T.v) + lo);
-      gload_lds16(kdt + (int64_t)d * S + 32 * kb + 8 * xt, reinterpret_cast<uint8_t*>(T.kt) + lo);
-    }
+    const int ci = tid, r = ci >> 4, x = (ci & 15) ^ (r & 15), d = ci >> 2, xt = (ci & 3) ^ ((d >> 2) & 3);
+    const int lo = 16 * (64 * wave_u);
+    gload_lds16(kd + (int64_t)(32 * kb + r) * 128 + 8 * x, reinterpret_cast<uint8_t*>(T.k) + lo);
+    gload_lds16(vd + (int64_t)(32 * kb + r) * 128 + 8 * x, reinterpret_cast<uint8_t*>(T.v) + lo);
+    gload_lds16(kdt + (int64_t)d * S + 32 * kb + 8 * xt, reinterpret_cast<uint8_t*>(T.kt) + lo);
   };
   // The K^T tile of "block -1" (the slot iteration 0 takes its dQ operands from) is zero: with zero dS
   // its products add exactly 0.
   {
     uint4* z = reinterpret_cast<uint4*>(buf[DQ_NBUF - 1].kt);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) z[256 * i + tid] = uint4{0u, 0u, 0u, 0u};
+    z[tid] = uint4{0u, 0u, 0u, 0u};
   }
   fetch(0, buf[0]);
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -674,9 +672,9 @@ hipError_t launch_attn_bwd(const uint8_t* qc, const uint8_t* qs, const uint8_t* 
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.qsb = qsb; p.qss = qss; p.qsh = qsh; p.ksb = ksb; p.kss = kss; p.ksh = ksh;
-  const unsigned tiles = (unsigned)((S + 127) / 128);
+  const unsigned tiles = (unsigned)((S + 127) / 128), dtiles = (unsigned)((S + 255) / 256);
   bwd_dkdv_kernel<<<dim3(tiles * (unsigned)Hkv * (unsigned)B), 256, 0, stream>>>(p);
-  bwd_dq_kernel<<<dim3(tiles * (unsigned)Hq * (unsigned)B), 256, 0, stream>>>(p);
+  bwd_dq_kernel<<<dim3(dtiles * (unsigned)Hq * (unsigned)B), 512, 0, stream>>>(p);
   return hipGetLastError();
 }
 
