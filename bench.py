@@ -130,9 +130,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa16x4_s32k_amplitudes")
-    ap.add_argument("--path", choices=["fused", "stepwise", "leaky"], default="fused",
+    ap.add_argument("--path", choices=["fused", "stepwise", "leaky", "mxfp8_out"], default="fused",
                     help="fused (default): the leak-free forward in one attention kernel; stepwise: its three "
-                         "separate kernels; leaky: ordinary causal MXFP8 (the variant the method replaces)")
+                         "separate kernels; leaky: ordinary causal MXFP8 (the variant the method replaces); "
+                         "mxfp8_out: the fused kernel with its output in MXFP8 (E4M3 codes + E8M0 per 32 columns)")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle CPU-baseline sample (0 skips)")
     ap.add_argument("--mode", choices=["fwd", "fwdbwd", "peak"], default="fwd",
                     help="fwd (default): the forward metric; fwdbwd: forward + bf16 backward on decoded operands "
@@ -183,6 +184,9 @@ def main():
     oc, lc = (torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)) if stepwise_buffers else (None, None)
     oo, lo = (torch.empty((B, Hq, S, D), **f32), torch.empty((B, Hq, S), **f32)) if stepwise_buffers else (None, None)
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    mx8 = args.path == "mxfp8_out"
+    out8 = torch.empty(q.shape, **u8) if mx8 else None  # E4M3 codes in O's layout
+    sf_o = torch.empty((B, Hq, S, D // 32), **u8) if mx8 else None
     lse = torch.empty((B, Hq, S), **f32)
     L = mx.lib()
     stream = torch.cuda.current_stream(dev)
@@ -192,12 +196,14 @@ def main():
     # The fused path quantises Q inside the attention kernel (attn_fwd_fused_bf16q, what attn_fwd runs);
     # the stepwise and leaky paths take Q's codes from the rowwise quantiser.
     names = (["quantize_k", "quantize_v", "fused"] if fused else
-             ["quantize_q", "quantize_k", "quantize_v"] + (["leaky"] if leaky else ["completed", "own_block", "merge"]))
+             ["quantize_q", "quantize_k", "quantize_v"] + (["leaky"] if leaky else ["fused_mxfp8"] if mx8 else
+                                                           ["completed", "own_block", "merge"]))
 
     def view(t):
         return mx.view_of(t, lay)
 
     qv, kv_, vv, ov = view(q), view(k), view(v), view(out)
+    ov8 = view(out8) if mx8 else None
 
     def step(evs=None):
         calls = [] if fused else [
@@ -213,6 +219,12 @@ def main():
             calls.append(lambda: L.mxfa_attn_fwd_leaky(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
                                                        vc.data_ptr(), vcs.data_ptr(), B, S, Hq, Hkv, D, w.scale,
                                                        out.data_ptr(), *ov[4:], mx.OUT_BF16, lse.data_ptr(), sh))
+        elif mx8:
+            calls.append(lambda: L.mxfa_attn_fwd_fused_mxfp8(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
+                                                             vc.data_ptr(), vcs.data_ptr(), vt.data_ptr(),
+                                                             vta.data_ptr(), B, S, Hq, Hkv, D, w.scale,
+                                                             out8.data_ptr(), *ov8[4:], sf_o.data_ptr(),
+                                                             lse.data_ptr(), sh))
         elif fused:
             calls.append(lambda: L.mxfa_attn_fwd_fused_bf16q(q.data_ptr(), *qv[4:], kc.data_ptr(), ks.data_ptr(),
                                                              vc.data_ptr(), vcs.data_ptr(), vt.data_ptr(),
@@ -256,8 +268,8 @@ def main():
     flops = 2.0 * B * Hq * S * S * D
     comp_flops = 512.0 * completed_pairs(B, Hq, S)
     own_flops = 512.0 * own_pairs(B, Hq, S)
-    attn_name = "fused" if fused else "leaky" if leaky else "completed"
-    attn_flops = comp_flops + own_flops if (fused or leaky) else comp_flops
+    attn_name = "fused" if fused else "leaky" if leaky else "fused_mxfp8" if mx8 else "completed"
+    attn_flops = comp_flops + own_flops if (fused or leaky or mx8) else comp_flops
     achieved = attn_flops / (per[attn_name] * 1e-3) / 1e12
     n_q, n_kv = B * Hq * S, B * Hkv * S
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
@@ -268,7 +280,7 @@ def main():
         "quantize_v": {"ms": per["quantize_v"],
                        "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32 + 1 + 1 / 128), per["quantize_v"])},
     }
-    if fused or leaky:
+    if fused or leaky or mx8:
         kernels[attn_name] = {"ms": per[attn_name], "TFLOP/s": achieved, "algorithmic_flop": attn_flops}
     else:
         kernels["completed"] = {"ms": per["completed"], "TFLOP/s": achieved, "algorithmic_flop": comp_flops}
@@ -294,7 +306,7 @@ def main():
         "dtype": "mxfp8",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "D": D, "layout": lay,
-                   "causal": True, "values": w.values, "output": "bf16", "path": args.path},
+                   "causal": True, "values": w.values, "output": "mxfp8" if mx8 else "bf16", "path": args.path},
         "pct_mfma_peak": round(100.0 * value / MFMA_FP8_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
