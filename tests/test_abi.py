@@ -28,6 +28,25 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_header_compiles_as_c_and_a_c_consumer_links(tmp_path):
+    """include/mxfa.h is plain C (C99, warnings as errors), and the C consumer of the GPU tests
+    (tests/c_abi/forward_from_c.c) links against libmxfa.so; the GPU test runs it."""
+    import subprocess
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    lib_dir, orc_dir = os.path.dirname(mx.LIB_PATH), os.path.join(ROOT, "oracle")
+    src = tmp_path / "h.c"
+    src.write_text('#include "mxfa.h"\nint main(void) { return mxfa_status_string(MXFA_OK) == 0; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    "-c", str(src), "-o", str(tmp_path / "h.o")], check=True, timeout=60)
+    if not os.path.exists(os.path.join(orc_dir, "liboracle.so")):
+        pytest.skip("oracle library not built")
+    subprocess.run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", orc_dir, "-I", os.path.join(rocm, "include"),
+                    os.path.join(ROOT, "tests", "c_abi", "forward_from_c.c"), "-L", lib_dir, "-lmxfa", "-L", orc_dir,
+                    "-loracle", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm", "-o", str(tmp_path / "ffc")],
+                   check=True, timeout=120)
+
+
 def test_library_exports_every_declared_symbol():
     lib = mx.lib()
     for n in declared_functions():
