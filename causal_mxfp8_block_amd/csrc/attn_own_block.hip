@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void own_block_kernel(const uint8_t* __restric
       so = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, so, 0, 0, 0);
     }
   }
-  __syncthreads();  // the decoded V rows are visible to the whole wave
+  __syncthreads();  // the decoded V^T is visible to the whole wave
   if (!valid) return;
   // Lane (c, hf), element i: key 8(i/4) + 4hf + i%4 of query c; softmax over keys <= c (log2 domain).
   const float scale_log2 = scale * 1.4426950408889634f;
