@@ -51,3 +51,34 @@ def test_random_shape_forward_and_own_block(case):
     goo = oo.double().cpu().numpy()
     assert report("own block", goo, roo, np.sqrt(np.mean(roo ** 2))) <= 1e-4
     assert np.max(np.abs(lo.double().cpu().numpy() - rlo)) < 1e-4
+
+
+def _bwd_cases(n=6, seed=7):
+    rng = np.random.default_rng(seed)
+    heads = [(1, 1), (2, 1), (3, 3), (4, 2), (4, 1), (6, 3)]
+    out = []
+    for i in range(n):
+        Hq, Hkv = heads[rng.integers(len(heads))]
+        out.append(dict(B=int(rng.integers(1, 3)), Hq=Hq, Hkv=Hkv, S=32 * int(rng.integers(1, 11)),
+                        layout=["bshd", "sbhd"][i % 2], values=["normal", "outliers", "token_amplitudes"][i % 3],
+                        seed=200 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _bwd_cases(), ids=lambda c: f"B{c['B']}_h{c['Hq']}x{c['Hkv']}_S{c['S']}_{c['layout']}_{c['values']}")
+def test_random_shape_backward(case):
+    """attn_bwd on random shapes (both layouts, GQA sums, all value mixes) against the oracle's fp64
+    backward, under the backward tests' gate (the R16 allowance plus the bf16 output rounding)."""
+    from test_gpu_backward import TOL as BTOL, _dout, _gate, _gpu_bwd, _stats_from_oracle, _view
+    w = custom(case["B"], case["Hq"], case["Hkv"], case["S"], layout=case["layout"], values=case["values"],
+               seed=case["seed"])
+    inp = make_inputs(w)
+    say(f"random backward {case}")
+    z = oracle.quantize_all(oracle_view(inp, "q"), oracle_view(inp, "k"), oracle_view(inp, "v"))
+    obits, lse = _stats_from_oracle(inp, z)
+    gbits = _dout(inp, case["seed"] + 1)
+    dq, dk, dv = _gpu_bwd(inp, obits, lse, gbits)
+    rq, rk, rv, aq, ak, av = oracle.attn_bwd(z.qc, z.qs, z.kc, z.ks, z.vt, z.vta, _view(obits, w.layout), lse,
+                                             _view(gbits, w.layout), w.scale, allowance=True)
+    for name, got, ref, al in (("dq", dq, rq, aq), ("dk", dk, rk, ak), ("dv", dv, rv, av)):
+        assert _gate(f"{name}", got, ref, al) <= BTOL
