@@ -82,3 +82,20 @@ def test_random_shape_backward(case):
                                              _view(gbits, w.layout), w.scale, allowance=True)
     for name, got, ref, al in (("dq", dq, rq, aq), ("dk", dk, rk, ak), ("dv", dv, rv, av)):
         assert _gate(f"{name}", got, ref, al) <= BTOL
+
+
+@pytest.mark.parametrize("case", _cases(n=4, seed=11),
+                         ids=lambda c: f"B{c['B']}_h{c['Hq']}x{c['Hkv']}_S{c['S']}_{c['layout']}_{c['values']}")
+def test_random_shape_leaky(case):
+    """The ordinary causal MXFP8 variant on random shapes against the oracle's leaky variant, under the
+    same gate (both half-tile positions of the own block occur)."""
+    from test_gpu_leaky import MAX_OVER as LMAX, TOL as LTOL, _gpu_leaky, _oracle_leaky
+    w = custom(case["B"], case["Hq"], case["Hkv"], case["S"], layout=case["layout"], values=case["values"],
+               seed=case["seed"])
+    inp = make_inputs(w)
+    say(f"random leaky {case}")
+    go, gl, _ = _gpu_leaky(inp)
+    ro, rl, A = _oracle_leaky(inp)
+    rms = np.sqrt(np.mean(ro ** 2))
+    gate("leaky", go, ro, rms, allowance=A.total, allowance_hw=A.code + A.pv, tol=LTOL, max_over_frac=LMAX)
+    assert np.max(np.abs(gl - rl)) < 1e-3
