@@ -195,8 +195,8 @@ def main():
     leaky = args.path == "leaky"
     # The fused path quantises Q inside the attention kernel (attn_fwd_fused_bf16q, what attn_fwd runs);
     # the stepwise and leaky paths take Q's codes from the rowwise quantiser.
-    names = (["quantize_k", "quantize_v", "fused"] if fused else
-             ["quantize_q", "quantize_k", "quantize_v"] + (["leaky"] if leaky else ["fused_mxfp8"] if mx8 else
+    names = (["quantize_kv", "fused"] if fused else
+             ["quantize_q", "quantize_kv"] + (["leaky"] if leaky else ["fused_mxfp8"] if mx8 else
                                                            ["completed", "own_block", "merge"]))
 
     def view(t):
@@ -209,12 +209,10 @@ def main():
         calls = [] if fused else [
             lambda: L.mxfa_mxfp8_quantize(q.data_ptr(), B, S, Hq, D, *qv[4:], mx.ROWWISE, qc.data_ptr(),
                                           qs.data_ptr(), None, None, sh)]
-        calls += [
-            lambda: L.mxfa_mxfp8_quantize(k.data_ptr(), B, S, Hkv, D, *kv_[4:], mx.ROWWISE, kc.data_ptr(),
-                                          ks.data_ptr(), None, None, sh),
-            lambda: L.mxfa_mxfp8_quantize(v.data_ptr(), B, S, Hkv, D, *vv[4:], mx.V, vc.data_ptr(), vcs.data_ptr(),
-                                          vt.data_ptr(), vta.data_ptr(), sh),
-        ]
+        # K and V in one launch, as attn_fwd encodes them
+        calls.append(lambda: L.mxfa_mxfp8_quantize_kv(k.data_ptr(), *kv_[4:], v.data_ptr(), *vv[4:], B, S, Hkv, D,
+                                                      kc.data_ptr(), ks.data_ptr(), vc.data_ptr(), vcs.data_ptr(),
+                                                      vt.data_ptr(), vta.data_ptr(), sh))
         if leaky:
             calls.append(lambda: L.mxfa_attn_fwd_leaky(qc.data_ptr(), qs.data_ptr(), kc.data_ptr(), ks.data_ptr(),
                                                        vc.data_ptr(), vcs.data_ptr(), B, S, Hq, Hkv, D, w.scale,
@@ -276,9 +274,8 @@ def main():
     kernels = {} if fused else {
         "quantize_q": {"ms": per["quantize_q"], "GB/s": gbs(n_q * D * (2 + 1 + 1 / 32), per["quantize_q"])}}
     kernels |= {
-        "quantize_k": {"ms": per["quantize_k"], "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32), per["quantize_k"])},
-        "quantize_v": {"ms": per["quantize_v"],
-                       "GB/s": gbs(n_kv * D * (2 + 1 + 1 / 32 + 1 + 1 / 128), per["quantize_v"])},
+        "quantize_kv": {"ms": per["quantize_kv"],
+                        "GB/s": gbs(n_kv * D * ((2 + 1 + 1 / 32) + (2 + 1 + 1 / 32 + 1 + 1 / 128)), per["quantize_kv"])},
     }
     if fused or leaky or mx8:
         kernels[attn_name] = {"ms": per[attn_name], "TFLOP/s": achieved, "algorithmic_flop": attn_flops}
@@ -344,8 +341,7 @@ def run_fwdbwd(args, torch, mx, WORKLOADS, make_inputs):
                 evs[i][j].record(stream)
         rec(0, 0)
         qc, qs = mx.mxfp8_quantize(q, "rowwise", lay)
-        kc, ks = mx.mxfp8_quantize(k, "rowwise", lay)
-        vc, vcs, vt, vta = mx.mxfp8_quantize(v, "v", lay)
+        kc, ks, vc, vcs, vt, vta = mx.mxfp8_quantize_kv(k, v, lay)
         rec(0, 1)
         rec(1, 0)
         o, lse = mx.attn_fwd_fused(qc, qs, kc, ks, vc, vcs, vt, vta, w.scale, layout=lay)

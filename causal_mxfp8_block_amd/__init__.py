@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L.mxfa_last_error.restype = ctypes.c_char_p
         L.mxfa_mxfp8_quantize.argtypes = [P, I, I, I, I, I64, I64, I64, I, P, P, P, P, P]
         L.mxfa_mxfp8_quantize.restype = I
+        L.mxfa_mxfp8_quantize_kv.argtypes = [P, I64, I64, I64] * 2 + [I, I, I, I] + [P] * 7
+        L.mxfa_mxfp8_quantize_kv.restype = I
         six = [P] * 6
         L.mxfa_attn_fwd_completed_blocks.argtypes = six + [I, I, I, I, I, F, P, P, P]
         L.mxfa_attn_fwd_completed_blocks.restype = I
@@ -132,6 +134,24 @@ def mxfp8_quantize(x: torch.Tensor, mode: str = "rowwise", layout: str = "bshd",
         _check(lib().mxfa_mxfp8_quantize(_p(x), B, S, H, D, sb, ss, sh, V, _p(cc), _p(cs), _p(tc), _p(ta), _stream(x)))
         return cc, cs, tc, ta
     raise ValueError(f"unknown mode {mode!r}")
+
+
+def mxfp8_quantize_kv(k: torch.Tensor, v: torch.Tensor, layout: str = "bshd"):
+    """K (rowwise) and V (both forms) in one launch, the bytes of mxfp8_quantize(k, "rowwise") and
+    mxfp8_quantize(v, "v"): returns (k_codes, k_scales, v_codes, v_scales, v_tn_codes, v_tn_amps)."""
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("k and v must be bfloat16")
+    B, S, H, D, ksb, kss, ksh = view_of(k, layout)
+    vB, vS, vH, vD, vsb, vss, vsh = view_of(v, layout)
+    if (vB, vS, vH, vD) != (B, S, H, D):
+        raise ValueError("k and v must have the same shape")
+    kw = dict(dtype=torch.uint8, device=k.device)
+    kc, ks = torch.empty((B, H, S, D), **kw), torch.empty((B, H, S, D // 32), **kw)
+    vc, vcs = torch.empty((B, H, D, S), **kw), torch.empty((B, H, S // 32, D), **kw)
+    vt, vta = torch.empty((B, H, S, D), **kw), torch.empty((B, H, S), **kw)
+    _check(lib().mxfa_mxfp8_quantize_kv(_p(k), ksb, kss, ksh, _p(v), vsb, vss, vsh, B, S, H, D, _p(kc), _p(ks),
+                                        _p(vc), _p(vcs), _p(vt), _p(vta), _stream(k)))
+    return kc, ks, vc, vcs, vt, vta
 
 
 def attn_fwd_completed_blocks(qc, qs, kc, ks, vc, vcs, softmax_scale: float | None = None, o_c=None, lse_c=None):

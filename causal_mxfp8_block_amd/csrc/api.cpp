@@ -211,6 +211,28 @@ MXFA_EXPORT int mxfa_mxfp8_quantize(const void* x, int B, int S, int H, int D, i
   return fail(MXFA_ERR_UNSUPPORTED, "unknown quantisation mode %d", mode);
 }
 
+MXFA_EXPORT int mxfa_mxfp8_quantize_kv(const void* k, int64_t ksb, int64_t kss, int64_t ksh, const void* v,
+                                       int64_t vsb, int64_t vss, int64_t vsh, int B, int S, int H, int D,
+                                       uint8_t* k_codes, uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales,
+                                       uint8_t* v_tn_codes, uint8_t* v_tn_amps, void* stream) {
+  g_last_error.clear();
+  if (D != 128) return fail(MXFA_ERR_UNSUPPORTED, "D = %d: only D = 128 is supported", D);
+  if (B < 1 || S < 1 || H < 1) return fail(MXFA_ERR_SHAPE, "B, S, H must be >= 1");
+  if (S > kMaxS) return fail(MXFA_ERR_SHAPE, "S = %d exceeds the largest supported length 2^24", S);
+  if (S % 32 != 0) return fail(MXFA_ERR_SHAPE, "S = %d is not a multiple of 32", S);
+  if (B > 65535 || H > 65535) return fail(MXFA_ERR_SHAPE, "B = %d, H = %d exceed the launch grid", B, H);
+  TRY(check_view("k", k, B, S, H, ksb, kss, ksh, 8));
+  TRY(check_view("v", v, B, S, H, vsb, vss, vsh, 8));
+  const char* n[] = {"k_codes", "k_scales", "v_codes", "v_scales", "v_tn_codes", "v_tn_amps"};
+  const void* p[] = {k_codes, k_scales, v_codes, v_scales, v_tn_codes, v_tn_amps};
+  TRY(check_ptrs(n, p, 6));
+  TRY(check_device());
+  return hip_status(mxfa::launch_quantize_kv(static_cast<const uint16_t*>(k), ksb, kss, ksh,
+                                             static_cast<const uint16_t*>(v), vsb, vss, vsh, B, S, H, k_codes, k_scales,
+                                             v_codes, v_scales, v_tn_codes, v_tn_amps, static_cast<hipStream_t>(stream)),
+                    "quantize_kv launch");
+}
+
 MXFA_EXPORT int mxfa_attn_fwd_completed_blocks(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc,
                                                const uint8_t* ks, const uint8_t* vc, const uint8_t* vcs, int B,
                                                int S, int Hq, int Hkv, int D, float softmax_scale, float* o_c,
@@ -369,8 +391,9 @@ MXFA_EXPORT int mxfa_attn_fwd(const void* q, int64_t qsb, int64_t qss, int64_t q
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t *q16 = static_cast<const uint16_t*>(q), *k16 = static_cast<const uint16_t*>(k),
                  *v16 = static_cast<const uint16_t*>(v);
-  TRY(hip_status(mxfa::launch_quantize_rowwise(k16, B, S, Hkv, ksb, kss, ksh, w.kc, w.ks, st), "quantize k"));
-  TRY(hip_status(mxfa::launch_quantize_v(v16, B, S, Hkv, vsb, vss, vsh, w.vc, w.vcs, w.vt, w.vta, st), "quantize v"));
+  TRY(hip_status(mxfa::launch_quantize_kv(k16, ksb, kss, ksh, v16, vsb, vss, vsh, B, S, Hkv, w.kc, w.ks, w.vc, w.vcs,
+                                          w.vt, w.vta, st),
+                 "quantize k and v"));
   return hip_status(mxfa::launch_attn_fused(nullptr, nullptr, w.kc, w.ks, w.vc, w.vcs, w.vt, w.vta, B, S, Hq, Hkv,
                                            softmax_scale, out, osb, oss, osh, out_dtype == MXFA_OUT_BF16, lse_out,
                                            st, nullptr, q16, qsb, qss, qsh),
@@ -402,8 +425,9 @@ MXFA_EXPORT int mxfa_attn_fwd_noalloc(const void* q, int64_t qsb, int64_t qss, i
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t *q16 = static_cast<const uint16_t*>(q), *k16 = static_cast<const uint16_t*>(k),
                  *v16 = static_cast<const uint16_t*>(v);
-  TRY(hip_status(mxfa::launch_quantize_rowwise(k16, B, S, Hkv, ksb, kss, ksh, w.kc, w.ks, st), "quantize k"));
-  TRY(hip_status(mxfa::launch_quantize_v(v16, B, S, Hkv, vsb, vss, vsh, w.vc, w.vcs, w.vt, w.vta, st), "quantize v"));
+  TRY(hip_status(mxfa::launch_quantize_kv(k16, ksb, kss, ksh, v16, vsb, vss, vsh, B, S, Hkv, w.kc, w.ks, w.vc, w.vcs,
+                                          w.vt, w.vta, st),
+                 "quantize k and v"));
   return hip_status(mxfa::launch_attn_fused(nullptr, nullptr, w.kc, w.ks, w.vc, w.vcs, w.vt, w.vta, B, S, Hq, Hkv,
                                            softmax_scale, out, osb, oss, osh, out_dtype == MXFA_OUT_BF16, lse_out,
                                            st, nullptr, q16, qsb, qss, qsh),

@@ -26,6 +26,9 @@ hipError_t launch_quantize_rowwise(const uint16_t* x, int B, int S, int H, int64
 hipError_t launch_quantize_v(const uint16_t* v, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
                              uint8_t* col_codes, uint8_t* col_scales, uint8_t* tn_codes, uint8_t* tn_amps,
                              hipStream_t stream);
+hipError_t launch_quantize_kv(const uint16_t* k, int64_t ksb, int64_t kss, int64_t ksh, const uint16_t* v,
+                              int64_t vsb, int64_t vss, int64_t vsh, int B, int S, int H, uint8_t* kc, uint8_t* ks,
+                              uint8_t* vc, uint8_t* vcs, uint8_t* vt, uint8_t* vta, hipStream_t stream);
 hipError_t launch_attn_completed(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
                                  const uint8_t* vc, const uint8_t* vcs, int B, int S, int Hq, int Hkv,
                                  float softmax_scale, float* o_c, float* lse_c, hipStream_t stream);

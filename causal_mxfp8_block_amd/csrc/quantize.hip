@@ -15,11 +15,10 @@ namespace mxfa {
 
 // One thread encodes one 32-element block (its four 16-byte loads in flight together), 4 threads a
 // D=128 row (9.6 us for K at 16/4 heads, S = 32K, against 11.0 with one thread per 8 elements).
-__global__ __launch_bounds__(256) void quantize_rowwise_kernel(const uint16_t* __restrict__ x, int S, int H,
-                                                               int64_t sb, int64_t ss, int64_t sh,
-                                                               uint8_t* __restrict__ codes,
-                                                               uint8_t* __restrict__ scales, int64_t nrows) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void rowwise_group(const uint16_t* __restrict__ x, int S, int H, int64_t sb, int64_t ss,
+                                              int64_t sh, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                              int64_t nrows, int64_t group) {
+  const int64_t gid = group * 256 + threadIdx.x;
   const int64_t row = gid >> 2;  // input row order (b, s, h)
   const int part = (int)(gid & 3);
   if (row >= nrows) return;
@@ -60,6 +59,13 @@ __global__ __launch_bounds__(256) void quantize_rowwise_kernel(const uint16_t* _
   scales[orow * 4 + part] = (uint8_t)(k + 127);
 }
 
+__global__ __launch_bounds__(256) void quantize_rowwise_kernel(const uint16_t* __restrict__ x, int S, int H,
+                                                               int64_t sb, int64_t ss, int64_t sh,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales, int64_t nrows) {
+  rowwise_group(x, S, H, sb, ss, sh, codes, scales, nrows, blockIdx.x);
+}
+
 // One workgroup per (b, h, group of up to 64 tokens): the bf16 tile is staged in LDS once and read
 // twice, by rows (token-normalised copy) and by columns (columnwise blocks). 64-token groups give
 // twice the workgroups of 128-token ones, so that one group's loads overlap another's conversions and
@@ -67,14 +73,12 @@ __global__ __launch_bounds__(256) void quantize_rowwise_kernel(const uint16_t* _
 constexpr int VQ_TOK = 64;
 constexpr int VQ_ROW = 128 + 8;  // bf16 elements per LDS row (padding spreads banks)
 
-__global__ __launch_bounds__(256) void quantize_v_kernel(const uint16_t* __restrict__ v, int S, int H, int64_t sb,
-                                                         int64_t ss, int64_t sh, uint8_t* __restrict__ col_codes,
-                                                         uint8_t* __restrict__ col_scales,
-                                                         uint8_t* __restrict__ tn_codes,
-                                                         uint8_t* __restrict__ tn_amps) {
-  __shared__ __align__(16) uint16_t tile[VQ_TOK * VQ_ROW];
+__device__ __forceinline__ void v_group(const uint16_t* __restrict__ v, int S, int H, int64_t sb, int64_t ss,
+                                        int64_t sh, uint8_t* __restrict__ col_codes, uint8_t* __restrict__ col_scales,
+                                        uint8_t* __restrict__ tn_codes, uint8_t* __restrict__ tn_amps,
+                                        uint16_t* tile, int group, int h, int b) {
   const int tid = threadIdx.x;
-  const int s0 = blockIdx.x * VQ_TOK, h = blockIdx.y, b = blockIdx.z;
+  const int s0 = group * VQ_TOK;
   const int ntok = min(VQ_TOK, S - s0);  // a multiple of 32
   const int64_t bh = (int64_t)b * H + h;
   // Thread tid moves chunk tid % 16 of rows tid / 16 + 16 i: all its loads are issued before any is
@@ -152,6 +156,37 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(const uint16_t* __restr
   }
 }
 
+__global__ __launch_bounds__(256) void quantize_v_kernel(const uint16_t* __restrict__ v, int S, int H, int64_t sb,
+                                                         int64_t ss, int64_t sh, uint8_t* __restrict__ col_codes,
+                                                         uint8_t* __restrict__ col_scales,
+                                                         uint8_t* __restrict__ tn_codes,
+                                                         uint8_t* __restrict__ tn_amps) {
+  __shared__ __align__(16) uint16_t tile[VQ_TOK * VQ_ROW];
+  v_group(v, S, H, sb, ss, sh, col_codes, col_scales, tn_codes, tn_amps, tile, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// K (rowwise) and V (both forms) of one attention call in one launch, the bytes of the two kernels
+// above: workgroups [0, nv) are V groups (token group g % ng, head (g / ng) % H, batch g / (ng H)),
+// the V groups first since each moves more than a K workgroup; the rest are K workgroups. One
+// dispatch instead of two, and the two encoders' workgroups share the machine.
+__global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __restrict__ k, int64_t ksb, int64_t kss,
+                                                          int64_t ksh, const uint16_t* __restrict__ v, int64_t vsb,
+                                                          int64_t vss, int64_t vsh, int S, int H, int ng, int64_t nv,
+                                                          int64_t nrows, uint8_t* __restrict__ kc,
+                                                          uint8_t* __restrict__ ks, uint8_t* __restrict__ vc,
+                                                          uint8_t* __restrict__ vcs, uint8_t* __restrict__ vt,
+                                                          uint8_t* __restrict__ vta) {
+  __shared__ __align__(16) uint16_t tile[VQ_TOK * VQ_ROW];
+  const int64_t g = blockIdx.x;
+  if (g < nv) {
+    const int gi = (int)(g % ng);
+    const int64_t bh = g / ng;
+    v_group(v, S, H, vsb, vss, vsh, vc, vcs, vt, vta, tile, gi, (int)(bh % H), (int)(bh / H));
+  } else {
+    rowwise_group(k, S, H, ksb, kss, ksh, kc, ks, nrows, g - nv);
+  }
+}
+
 hipError_t launch_quantize_rowwise(const uint16_t* x, int B, int S, int H, int64_t sb, int64_t ss, int64_t sh,
                                    uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   const int64_t nrows = (int64_t)B * S * H;
@@ -166,6 +201,18 @@ hipError_t launch_quantize_v(const uint16_t* v, int B, int S, int H, int64_t sb,
                              hipStream_t stream) {
   dim3 grid((unsigned)((S + VQ_TOK - 1) / VQ_TOK), (unsigned)H, (unsigned)B);
   quantize_v_kernel<<<grid, dim3(256), 0, stream>>>(v, S, H, sb, ss, sh, col_codes, col_scales, tn_codes, tn_amps);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_kv(const uint16_t* k, int64_t ksb, int64_t kss, int64_t ksh, const uint16_t* v,
+                              int64_t vsb, int64_t vss, int64_t vsh, int B, int S, int H, uint8_t* kc, uint8_t* ks,
+                              uint8_t* vc, uint8_t* vcs, uint8_t* vt, uint8_t* vta, hipStream_t stream) {
+  const int ng = (S + VQ_TOK - 1) / VQ_TOK;
+  const int64_t nv = (int64_t)ng * H * B;
+  const int64_t nrows = (int64_t)B * S * H;
+  const int64_t nk = (nrows * 4 + 255) / 256;
+  quantize_kv_kernel<<<dim3((unsigned)(nv + nk)), dim3(256), 0, stream>>>(k, ksb, kss, ksh, v, vsb, vss, vsh, S, H, ng,
+                                                                         nv, nrows, kc, ks, vc, vcs, vt, vta);
   return hipGetLastError();
 }
 

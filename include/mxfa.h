@@ -72,6 +72,17 @@ int mxfa_mxfp8_quantize(const void* x_bf16, int B, int S, int H, int D, int64_t 
                         int mode, uint8_t* codes, uint8_t* scales, uint8_t* tn_codes, uint8_t* tn_amps,
                         void* stream);
 
+/* mxfp8_quantize_kv -- the K and V encodings of one attention call in one launch: K as mode ROWWISE
+ * and V as mode V with both outputs, the same bytes as those two mxfp8_quantize calls (TE #3865
+ * Description: rowwise K; columnwise V blocks over 32 tokens plus the token-normalised copy). K and V
+ * are [B,S,H,D] bf16 views with their own strides; S % 32 == 0; every output is required:
+ * k_codes [B,H,S,D], k_scales [B,H,S,D/32], v_codes [B,H,D,S], v_scales [B,H,S/32,D],
+ * v_tn_codes [B,H,S,D], v_tn_amps [B,H,S]. One dispatch instead of two; attn_fwd runs it. */
+int mxfa_mxfp8_quantize_kv(const void* k_bf16, int64_t ksb, int64_t kss, int64_t ksh, const void* v_bf16,
+                           int64_t vsb, int64_t vss, int64_t vsh, int B, int S, int H, int D, uint8_t* k_codes,
+                           uint8_t* k_scales, uint8_t* v_codes, uint8_t* v_scales, uint8_t* v_tn_codes,
+                           uint8_t* v_tn_amps, void* stream);
+
 /* attn_fwd_completed_blocks -- the completed-block partial (TE #3865 Description, first bullet):
  * for every (b, hq, i), keys j < 32*floor(i/32). Scores t = softmax_scale*log2(e)*(Q^_i . K^_j) come
  * from block-scaled FP8 products; p = 2^(t - T) with an integer running exponent T; P is quantised

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["mxfa_mxfp8_quantize", "mxfa_attn_fwd_completed_blocks", "mxfa_attn_fwd_own_block",
+    for n in ["mxfa_mxfp8_quantize", "mxfa_mxfp8_quantize_kv", "mxfa_attn_fwd_completed_blocks", "mxfa_attn_fwd_own_block",
               "mxfa_lse_merge", "mxfa_attn_fwd", "mxfa_attn_fwd_fused", "mxfa_attn_fwd_leaky",
               "mxfa_attn_fwd_workspace_bytes",
               "mxfa_status_string",
@@ -94,6 +94,21 @@ def test_quantize_validation():
     assert st == 3 and "token-normalised" in msg
     st, msg = _err(L.mxfa_mxfp8_quantize(FAKE, 1, 40, 2, 128, 40 * 256, 256, 128, 1, FAKE, FAKE, None, None, None))
     assert st == 2
+
+
+def test_quantize_kv_validation():
+    L = mx.lib()
+    ok = (FAKE, 64 * 256, 256, 128)
+    st, msg = _err(L.mxfa_mxfp8_quantize_kv(*ok, *ok, 1, 64, 2, 64, *[FAKE] * 6, None))
+    assert st == 3 and "D = 64" in msg
+    st, msg = _err(L.mxfa_mxfp8_quantize_kv(*ok, *ok, 1, 40, 2, 128, *[FAKE] * 6, None))
+    assert st == 2 and "multiple of 32" in msg
+    st, msg = _err(L.mxfa_mxfp8_quantize_kv(*ok, *ok, 1, (1 << 24) + 32, 2, 128, *[FAKE] * 6, None))
+    assert st == 2 and "2^24" in msg
+    st, msg = _err(L.mxfa_mxfp8_quantize_kv(*ok, FAKE, 64 * 256, 256, 12, 1, 64, 2, 128, *[FAKE] * 6, None))
+    assert st in (2, 4)
+    st, msg = _err(L.mxfa_mxfp8_quantize_kv(*ok, *ok, 1, 64, 2, 128, *[FAKE] * 5, None, None))
+    assert st == 1 and "v_tn_amps" in msg
 
 
 def test_merge_and_forward_validation():

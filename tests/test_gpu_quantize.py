@@ -78,3 +78,28 @@ def test_quantize_ragged_and_strided():
     ref = oracle.quantize_v(inp.v)
     for a, b in zip(out, ref):
         assert np.array_equal(a.cpu().numpy(), b)
+
+
+@pytest.mark.parametrize("B,S,H,layout", [(1, 32, 1, "bshd"), (2, 96, 3, "bshd"), (1, 160, 4, "sbhd"),
+                                          (1, 32768, 4, "bshd")])
+def test_quantize_kv_equals_separate_calls_and_oracle(B, S, H, layout):
+    """mxfp8_quantize_kv (one launch, what attn_fwd runs) = mxfp8_quantize(k, rowwise) and
+    mxfp8_quantize(v, v) byte for byte, K and V from different strided views (token groups of 64 with
+    a ragged last one at S = 96 and 160), and the oracle's encoders on the same inputs."""
+    from causal_mxfp8_block_amd.inputs import custom
+    inp = make_inputs(custom(B, 2 * H, H, S, layout=layout, values="token_amplitudes", seed=40 + S + H))
+    say(f"quantize_kv B={B} S={S} H={H} {layout}")
+    kfull, vfull = to_dev(inp.k), to_dev(inp.v)
+    # K and V as views into wider tensors with different strides
+    kwide = torch.zeros(kfull.shape[:-2] + (H + 1, 128), dtype=torch.bfloat16, device=kfull.device)
+    kwide[..., 1:, :] = kfull
+    k = kwide[..., 1:, :]
+    got = mx.mxfp8_quantize_kv(k, vfull, layout)
+    torch.cuda.synchronize()
+    ref = list(mx.mxfp8_quantize(k, "rowwise", layout)) + list(mx.mxfp8_quantize(vfull, "v", layout))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("kc", "ks", "vc", "vcs", "vt", "vta"), got, ref):
+        assert torch.equal(a, b), name
+    ok = oracle.quantize_rowwise(oracle_view(inp, "k")) + oracle.quantize_v(oracle_view(inp, "v"))
+    for name, a, b in zip(("kc", "ks", "vc", "vcs", "vt", "vta"), got, ok):
+        assert np.array_equal(a.cpu().numpy(), b), name
