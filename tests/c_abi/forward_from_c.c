@@ -2,9 +2,10 @@
  * forward_from_c.c -- a plain C consumer of libmxfa (include/mxfa.h), with no Python in the loop.
  *
  * For seeded N(0,1) bf16 inputs (B=1, 2 query heads, 1 KV head, D=128) it
- *   1. encodes Q, K (rowwise) and V (columnwise + token-normalised) with mxfa_mxfp8_quantize and checks
- *      every code and scale byte against the oracle's encoders (TransformerEngine PR #3865,
- *      "Description": rowwise Q/K, columnwise V over 32 tokens, one amplitude per token);
+ *   1. encodes Q, K (rowwise) and V (columnwise + token-normalised) with mxfa_mxfp8_quantize, and K
+ *      and V again in one launch with mxfa_mxfp8_quantize_kv, and checks every code and scale byte
+ *      against the oracle's encoders (TransformerEngine PR #3865, "Description": rowwise Q/K,
+ *      columnwise V over 32 tokens, one amplitude per token);
  *   2. runs the whole forward, mxfa_attn_fwd, and checks it equals the chain of separate entry points
  *      (the three quantisations, then mxfa_attn_fwd_fused) bit for bit, as the header promises;
  *   3. at S = 32, where every query has only its own block (no quantised P), checks the own-block
@@ -113,6 +114,25 @@ static void run_case(int S) {
     void* h = host_copy(enc[i].dev, enc[i].n);
     expect_equal(enc[i].name, h, enc[i].ref, enc[i].n, S);
     free(h);
+  }
+  /* ... and K and V in one launch (what mxfa_attn_fwd runs): the same bytes */
+  {
+    void *ekc = dev_alloc(nk), *eks = dev_alloc(ksn), *evc = dev_alloc(nk), *evcs = dev_alloc(ksn);
+    void *evt = dev_alloc(nk), *evta = dev_alloc((size_t)B * Hkv * S);
+    MX_OK(mxfa_mxfp8_quantize_kv(dk, ksb, kss, ksh, dv, ksb, kss, ksh, B, S, Hkv, D, ekc, eks, evc, evcs, evt, evta,
+                                 NULL));
+    HIP_OK(hipDeviceSynchronize());
+    struct { const char* name; void* dev; uint8_t* ref; size_t n; } kv[] = {
+        {"quantize_kv: K codes", ekc, okc, nk}, {"quantize_kv: K scales", eks, oks, ksn},
+        {"quantize_kv: V columnwise codes", evc, ovc, nk}, {"quantize_kv: V columnwise scales", evcs, ovcs, ksn},
+        {"quantize_kv: V token-normalised codes", evt, ovt, nk},
+        {"quantize_kv: V token amplitudes", evta, ovta, (size_t)B * Hkv * S}};
+    for (size_t i = 0; i < sizeof(kv) / sizeof(kv[0]); ++i) {
+      void* h = host_copy(kv[i].dev, kv[i].n);
+      expect_equal(kv[i].name, h, kv[i].ref, kv[i].n, S);
+      free(h);
+      HIP_OK(hipFree(kv[i].dev));
+    }
   }
 
   /* 2. the whole forward against the chain of separate calls */
