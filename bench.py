@@ -1,9 +1,10 @@
 """Benchmark: leak-free causal MXFP8 attention forward on one MI355X.
 
 One step is one pass of the whole forward path over one batch: MXFP8 quantisation of Q, K (rowwise)
-and V (columnwise + token-normalised), then the completed-block partial, the own-block partial and
-the LSE merge (bf16 output) -- by default in one fused kernel (`--path fused`), or as three separate
-kernels (`--path stepwise`) -- each call through the C ABI of libmxfa.so on torch's current stream.
+and V (columnwise + token-normalised; K and V in one launch), then the completed-block partial, the
+own-block partial and the LSE merge (bf16 output) -- by default in one fused kernel that also
+quantises Q (`--path fused`), or as three separate kernels after a separate Q quantiser
+(`--path stepwise`) -- each call through the C ABI of libmxfa.so on torch's current stream.
 `--path leaky` times ordinary causal MXFP8 instead (the variant the method replaces), for the
 own-block/ordinary comparison the published timings make.
 Inputs are seeded synthetic bf16 tensors already resident in HBM when the timed region starts.
